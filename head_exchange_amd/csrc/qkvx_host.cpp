@@ -1,0 +1,510 @@
+// Host side of the C ABI: argument validation, sessions, receive-slot cycling
+// and kernel launches.  Every check runs before anything is enqueued, so a call
+// that fails leaves every buffer as it was (the pages' contract: invalid calls
+// raise before any launch or collective).
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <string>
+
+#include "qkvx_internal.h"
+
+using namespace qkvx;
+
+namespace {
+
+thread_local std::string g_error;
+
+int fail(int status, const char* fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof(buf), fmt, ap);
+    va_end(ap);
+    g_error = buf;
+    return status;
+}
+
+int ok() {
+    g_error.clear();
+    return QKVX_OK;
+}
+
+int hip_fail(hipError_t e, const char* what) {
+    return fail(QKVX_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+constexpr int64_t kInt32Limit = int64_t(1) << 31;
+constexpr int64_t kUint32Limit = int64_t(1) << 32;
+constexpr uint16_t kPoison = 0x7FC1;
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Byte range [lo, hi) covered by a strided bf16 view.
+struct Range {
+    uintptr_t lo, hi;
+};
+Range view_range(const void* base, const int64_t* shape, const int64_t* stride, int dims) {
+    int64_t last = 0;
+    for (int i = 0; i < dims; ++i) last += (shape[i] - 1) * stride[i];
+    uintptr_t lo = reinterpret_cast<uintptr_t>(base);
+    return Range{lo, lo + uintptr_t(last + 1) * 2};
+}
+Range bytes_range(const void* base, int64_t bytes) {
+    uintptr_t lo = reinterpret_cast<uintptr_t>(base);
+    return Range{lo, lo + uintptr_t(bytes)};
+}
+bool overlap(Range a, Range b) { return a.lo < b.hi && b.lo < a.hi; }
+
+// Schedule checks shared by pack and merge: counts > 0 summing to local_heads.
+int check_schedule(const int* schedule, int n_chunks, int chunk, int local_heads, int* off,
+                   int* count) {
+    if (!schedule) return fail(QKVX_ERR_INVALID, "schedule is NULL");
+    if (n_chunks < 1) return fail(QKVX_ERR_INVALID, "n_chunks must be >= 1 (got %d)", n_chunks);
+    if (chunk < 0 || chunk >= n_chunks)
+        return fail(QKVX_ERR_INVALID, "chunk %d outside [0, %d)", chunk, n_chunks);
+    int64_t sum = 0;
+    int o = 0;
+    for (int i = 0; i < n_chunks; ++i) {
+        if (schedule[i] <= 0)
+            return fail(QKVX_ERR_DIVISIBILITY, "schedule[%d] = %d must be > 0", i, schedule[i]);
+        if (i < chunk) o += schedule[i];
+        sum += schedule[i];
+    }
+    if (sum != local_heads)
+        return fail(QKVX_ERR_DIVISIBILITY, "schedule sums to %lld, local heads are %d",
+                    (long long)sum, local_heads);
+    *off = o;
+    *count = schedule[chunk];
+    return QKVX_OK;
+}
+
+int check_peers(const qkvx_peers* p, const char* name, int world, int64_t batch, int64_t s,
+                int head_count, int64_t inner) {
+    if (!p) return fail(QKVX_ERR_INVALID, "%s is NULL", name);
+    if (p->world != world)
+        return fail(QKVX_ERR_INVALID, "%s.world = %d, expected %d", name, p->world, world);
+    if (p->batch < batch)
+        return fail(QKVX_ERR_CAPACITY, "%s.batch = %lld < batch %lld", name, (long long)p->batch,
+                    (long long)batch);
+    if (p->row_offset < 0 || p->head_offset < 0)
+        return fail(QKVX_ERR_INVALID, "%s offsets must be >= 0", name);
+    if (p->rows < p->row_offset + s)
+        return fail(QKVX_ERR_CAPACITY, "%s rows %lld < row_offset %lld + %lld", name,
+                    (long long)p->rows, (long long)p->row_offset, (long long)s);
+    if (p->heads < p->head_offset + head_count)
+        return fail(QKVX_ERR_CAPACITY, "%s heads %lld < head_offset %lld + %d", name,
+                    (long long)p->heads, (long long)p->head_offset, head_count);
+    for (int i = 0; i < 3; ++i) {
+        if (p->stride[i] <= 0)
+            return fail(QKVX_ERR_LAYOUT, "%s.stride[%d] = %lld must be > 0", name, i,
+                        (long long)p->stride[i]);
+        if (p->stride[i] % 8)
+            return fail(QKVX_ERR_ALIGNMENT, "%s.stride[%d] = %lld is not a multiple of 8 elements",
+                        name, i, (long long)p->stride[i]);
+    }
+    if (p->stride[2] < inner)
+        return fail(QKVX_ERR_LAYOUT, "%s.stride[2] = %lld < %lld (heads would overlap)", name,
+                    (long long)p->stride[2], (long long)inner);
+    const int64_t extent = (p->batch - 1) * p->stride[0] + (p->rows - 1) * p->stride[1] +
+                           (p->heads - 1) * p->stride[2] + inner;
+    if (extent >= kInt32Limit)
+        return fail(QKVX_ERR_INT32_RANGE, "%s spans %lld elements (limit 2^31)", name,
+                    (long long)extent);
+    for (int u = 0; u < world; ++u) {
+        if (!p->base[u]) return fail(QKVX_ERR_INVALID, "%s.base[%d] is NULL", name, u);
+        if (!aligned16(p->base[u]))
+            return fail(QKVX_ERR_ALIGNMENT, "%s.base[%d] is not 16-byte aligned", name, u);
+    }
+    return QKVX_OK;
+}
+
+// Byte range of the elements a call touches in peer u.
+Range peers_touched(const qkvx_peers* p, int u, int64_t batch, int64_t s, int head_count,
+                    int64_t inner) {
+    const int64_t first = p->row_offset * p->stride[1] + p->head_offset * p->stride[2];
+    const int64_t last = first + (batch - 1) * p->stride[0] + (s - 1) * p->stride[1] +
+                         (head_count - 1) * p->stride[2] + inner - 1;
+    uintptr_t b = reinterpret_cast<uintptr_t>(p->base[u]);
+    return Range{b + uintptr_t(first) * 2, b + uintptr_t(last + 1) * 2};
+}
+
+}  // namespace
+
+// ===========================================================================
+// session
+// ===========================================================================
+
+struct qkvx_session {
+    int hidden, heads, world, layout, num_slots;
+    int64_t max_tokens;
+    int64_t region_elems;       // max_tokens * 3 * hidden
+    uint16_t* slots;            // num_slots * world regions
+    size_t slot_bytes;
+    bool owns_slots;
+    int64_t calls;              // successful forward calls so far
+    bool has_last;
+    qkvx_outputs last;
+};
+
+extern "C" {
+
+const char* qkvx_last_error(void) { return g_error.c_str(); }
+
+size_t qkvx_slot_bytes(int hidden, int world, int64_t max_tokens, int num_slots) {
+    if (hidden <= 0 || world <= 0 || max_tokens <= 0 || num_slots <= 0) return 0;
+    return size_t(num_slots) * size_t(world) * size_t(max_tokens) * 3u * size_t(hidden) * 2u;
+}
+
+int qkvx_create(int hidden, int num_heads, int head_dim, int world, int layout,
+                int64_t max_tokens, int num_slots, void* slot_memory, size_t slot_bytes,
+                qkvx_session** out) {
+    if (!out) return fail(QKVX_ERR_INVALID, "out is NULL");
+    *out = nullptr;
+    if (head_dim != QKVX_HEAD_DIM)
+        return fail(QKVX_ERR_INVALID, "head_dim must be %d (got %d)", QKVX_HEAD_DIM, head_dim);
+    if (num_heads <= 0) return fail(QKVX_ERR_INVALID, "num_heads must be > 0");
+    if (hidden != num_heads * head_dim)
+        return fail(QKVX_ERR_INVALID, "hidden %d != num_heads %d * head_dim %d", hidden,
+                    num_heads, head_dim);
+    if (world < 1 || world > QKVX_MAX_WORLD)
+        return fail(QKVX_ERR_INVALID, "world %d outside [1, %d]", world, QKVX_MAX_WORLD);
+    if (num_heads % world)
+        return fail(QKVX_ERR_DIVISIBILITY, "num_heads %d is not divisible by world %d",
+                    num_heads, world);
+    if (layout != QKVX_LAYOUT_BSHD && layout != QKVX_LAYOUT_FUSED)
+        return fail(QKVX_ERR_LAYOUT, "layout %d is neither bshd (0) nor fused (1)", layout);
+    if (max_tokens < 1) return fail(QKVX_ERR_INVALID, "max_tokens must be >= 1");
+    if (num_slots < 1) return fail(QKVX_ERR_INVALID, "num_slots must be >= 1");
+    // operands: x [M, hidden], W [3 hidden, hidden]; byte offsets of padded
+    // tiles stay below 2^32, element extents below 2^31.
+    const int64_t w_elems = int64_t(3) * hidden * hidden;
+    const int64_t x_elems = max_tokens * hidden;
+    const int64_t region = max_tokens * 3 * int64_t(hidden);
+    if (w_elems >= kInt32Limit || (int64_t(3) * hidden + 256) * hidden * 2 >= kUint32Limit)
+        return fail(QKVX_ERR_INT32_RANGE, "W_qkv [%d, %d] exceeds the 2^31-element limit",
+                    3 * hidden, hidden);
+    if (x_elems >= kInt32Limit || (max_tokens + 256) * hidden * 2 >= kUint32Limit)
+        return fail(QKVX_ERR_INT32_RANGE, "max_tokens %lld x hidden %d exceeds the 2^31 limit",
+                    (long long)max_tokens, hidden);
+    if (region >= kInt32Limit)
+        return fail(QKVX_ERR_INT32_RANGE, "a receive region of %lld elements exceeds 2^31",
+                    (long long)region);
+    const size_t need = qkvx_slot_bytes(hidden, world, max_tokens, num_slots);
+    bool owns = false;
+    if (slot_memory) {
+        if (slot_bytes < need)
+            return fail(QKVX_ERR_CAPACITY, "slot_memory holds %zu bytes, %zu needed", slot_bytes,
+                        need);
+        if (reinterpret_cast<uintptr_t>(slot_memory) & 255u)
+            return fail(QKVX_ERR_ALIGNMENT, "slot_memory is not 256-byte aligned");
+    } else {
+        hipError_t e = hipMalloc(&slot_memory, need);
+        if (e != hipSuccess) return hip_fail(e, "hipMalloc of the receive slots");
+        slot_bytes = need;
+        owns = true;
+    }
+    qkvx_session* s = new qkvx_session();
+    s->hidden = hidden;
+    s->heads = num_heads;
+    s->world = world;
+    s->layout = layout;
+    s->num_slots = num_slots;
+    s->max_tokens = max_tokens;
+    s->region_elems = region;
+    s->slots = static_cast<uint16_t*>(slot_memory);
+    s->slot_bytes = slot_bytes;
+    s->owns_slots = owns;
+    s->calls = 0;
+    s->has_last = false;
+    *out = s;
+    return ok();
+}
+
+int qkvx_destroy(qkvx_session* s) {
+    if (!s) return fail(QKVX_ERR_INVALID, "session is NULL");
+    if (s->owns_slots) {
+        hipError_t e = hipFree(s->slots);
+        delete s;
+        if (e != hipSuccess) return hip_fail(e, "hipFree of the receive slots");
+        return ok();
+    }
+    delete s;
+    return ok();
+}
+
+static void fill_outputs(const qkvx_session* s, int slot, int batch, int s_local, int rank,
+                         qkvx_outputs* o) {
+    memset(o, 0, sizeof(*o));
+    const int64_t hl = s->heads / s->world;
+    const int64_t sg = int64_t(s->world) * s_local;
+    o->slot = slot;
+    o->world = s->world;
+    o->layout = s->layout;
+    o->rank = rank;
+    o->batch = batch;
+    o->s_global = sg;
+    o->local_heads = hl;
+    o->head_dim = QKVX_HEAD_DIM;
+    const int64_t inner = s->layout == QKVX_LAYOUT_BSHD ? 128 : 384;
+    o->stride[3] = 1;
+    o->stride[2] = inner;
+    o->stride[1] = hl * inner;
+    o->stride[0] = sg * hl * inner;
+    const int64_t part = s->layout == QKVX_LAYOUT_BSHD ? batch * sg * hl * 128 : 128;
+    for (int d = 0; d < s->world; ++d) {
+        uint16_t* base = s->slots + (int64_t(slot) * s->world + d) * s->region_elems;
+        o->q[d] = base;
+        o->k[d] = base + part;
+        o->v[d] = base + 2 * part;
+    }
+}
+
+int qkvx_forward(qkvx_session* s, const void* x, int batch, int s_local, const void* w_qkv,
+                 const float* q_norm_w, const float* k_norm_w, const float* cos_sin,
+                 int64_t cos_sin_rows, int rank, void* stream, qkvx_outputs* out) {
+    if (!s) return fail(QKVX_ERR_INVALID, "session is NULL");
+    if (!x || !w_qkv || !q_norm_w || !k_norm_w || !cos_sin)
+        return fail(QKVX_ERR_INVALID, "x, w_qkv, q_norm_w, k_norm_w and cos_sin must be non-NULL");
+    if (batch < 1 || s_local < 1)
+        return fail(QKVX_ERR_INVALID, "batch %d and s_local %d must be >= 1", batch, s_local);
+    const int64_t M = int64_t(batch) * s_local;
+    if (M > s->max_tokens)
+        return fail(QKVX_ERR_CAPACITY, "batch * s_local = %lld exceeds max_tokens %lld",
+                    (long long)M, (long long)s->max_tokens);
+    if (rank < 0 || rank >= s->world)
+        return fail(QKVX_ERR_INVALID, "rank %d outside [0, %d)", rank, s->world);
+    if (cos_sin_rows < int64_t(rank + 1) * s_local)
+        return fail(QKVX_ERR_CAPACITY, "cos_sin has %lld rows, positions up to %lld are needed",
+                    (long long)cos_sin_rows, (long long)(int64_t(rank + 1) * s_local));
+    if (cos_sin_rows * 128 >= kInt32Limit)
+        return fail(QKVX_ERR_INT32_RANGE, "cos_sin table exceeds 2^31 elements");
+    if (!aligned16(x) || !aligned16(w_qkv))
+        return fail(QKVX_ERR_ALIGNMENT, "x and w_qkv must start at 16-byte aligned addresses");
+    if (!aligned16(q_norm_w) || !aligned16(k_norm_w) || !aligned16(cos_sin))
+        return fail(QKVX_ERR_ALIGNMENT,
+                    "cos_sin and the norm weights must start at 16-byte aligned addresses");
+    const int64_t hidden = s->hidden;
+    const Range slots = bytes_range(s->slots, int64_t(s->slot_bytes));
+    const Range ins[5] = {bytes_range(x, M * hidden * 2), bytes_range(w_qkv, 3 * hidden * hidden * 2),
+                          bytes_range(q_norm_w, 512), bytes_range(k_norm_w, 512),
+                          bytes_range(cos_sin, cos_sin_rows * 512)};
+    const char* names[5] = {"x", "w_qkv", "q_norm_w", "k_norm_w", "cos_sin"};
+    for (int i = 0; i < 5; ++i)
+        if (overlap(slots, ins[i]))
+            return fail(QKVX_ERR_ALIAS, "%s overlaps the session's receive slots", names[i]);
+
+    const int slot = int(s->calls % s->num_slots);
+    qkvx_outputs o;
+    fill_outputs(s, slot, batch, s_local, rank, &o);
+
+    FusedArgs a;
+    memset(&a, 0, sizeof(a));
+    a.x = static_cast<const uint16_t*>(x);
+    a.w = static_cast<const uint16_t*>(w_qkv);
+    a.wq = q_norm_w;
+    a.wk = k_norm_w;
+    a.cs = cos_sin;
+    a.slot = static_cast<uint16_t*>(o.q[0]);
+    a.region_elems = s->region_elems;
+    a.part_stride = static_cast<uint16_t*>(o.k[0]) - static_cast<uint16_t*>(o.q[0]);
+    a.stride_b = o.stride[0];
+    a.stride_s = o.stride[1];
+    a.stride_h = o.stride[2];
+    a.M = int32_t(M);
+    a.N = int32_t(3 * hidden);
+    a.K = int32_t(hidden);
+    a.hidden = int32_t(hidden);
+    a.local_heads = s->heads / s->world;
+    a.s_local = s_local;
+    a.row0 = rank * s_local;
+    a.eps = 1e-6f;
+    hipError_t e = launch_fused(a, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "fused projection launch");
+    s->calls += 1;
+    s->last = o;
+    s->has_last = true;
+    if (out) *out = o;
+    return ok();
+}
+
+int qkvx_last_outputs(const qkvx_session* s, qkvx_outputs* out) {
+    if (!s || !out) return fail(QKVX_ERR_INVALID, "session and out must be non-NULL");
+    if (!s->has_last) return fail(QKVX_ERR_INVALID, "no call has been made on this session");
+    *out = s->last;
+    return ok();
+}
+
+int qkvx_poison_receive_slots(qkvx_session* s, void* stream) {
+    if (!s) return fail(QKVX_ERR_INVALID, "session is NULL");
+    const int64_t n = int64_t(s->num_slots) * s->world * s->region_elems;
+    hipError_t e = launch_fill16(s->slots, n, kPoison, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "poison fill launch");
+    return ok();
+}
+
+int qkvx_describe(const qkvx_session* s, char* buf, size_t len) {
+    if (!s) return fail(QKVX_ERR_INVALID, "session is NULL");
+    const FusedPlan p = fused_plan();
+    char tmp[1024];
+    int n = snprintf(
+        tmp, sizeof(tmp),
+        "{\"hidden\": %d, \"num_heads\": %d, \"head_dim\": %d, \"world\": %d, "
+        "\"local_heads\": %d, \"layout\": \"%s\", \"max_tokens\": %lld, \"num_slots\": %d, "
+        "\"region_elems\": %lld, \"slot_bytes\": %zu, \"owns_slots\": %s, \"calls\": %lld, "
+        "\"next_slot\": %d, \"rope\": \"rotate_half\", \"eps\": 1e-6, "
+        "\"tile\": {\"block_m\": %d, \"block_n\": %d, \"block_k\": %d, \"threads\": %d, "
+        "\"group_m\": %d, \"mfma\": \"v_mfma_f32_32x32x16_bf16\", \"xcd_remap\": 8}}",
+        s->hidden, s->heads, QKVX_HEAD_DIM, s->world, s->heads / s->world,
+        s->layout == QKVX_LAYOUT_BSHD ? "bshd" : "fused", (long long)s->max_tokens,
+        s->num_slots, (long long)s->region_elems, s->slot_bytes, s->owns_slots ? "true" : "false",
+        (long long)s->calls, int(s->calls % s->num_slots), p.block_m, p.block_n, p.block_k,
+        p.threads, p.group_m);
+    if (buf && len) {
+        size_t c = size_t(n) < len ? size_t(n) : len - 1;
+        memcpy(buf, tmp, c);
+        buf[c] = 0;
+    }
+    g_error.clear();
+    return n;
+}
+
+// ===========================================================================
+// head-chunk transport
+// ===========================================================================
+
+static int check_view(const qkvx_view4* v, const char* name) {
+    if (!v) return fail(QKVX_ERR_INVALID, "%s is NULL", name);
+    if (!v->base) return fail(QKVX_ERR_INVALID, "%s.base is NULL", name);
+    for (int i = 0; i < 4; ++i)
+        if (v->shape[i] < 1)
+            return fail(QKVX_ERR_INVALID, "%s.shape[%d] = %lld must be >= 1", name, i,
+                        (long long)v->shape[i]);
+    if (v->shape[3] != QKVX_HEAD_DIM)
+        return fail(QKVX_ERR_INVALID, "%s head_dim %lld != 128", name, (long long)v->shape[3]);
+    if (v->stride[3] != 1)
+        return fail(QKVX_ERR_LAYOUT, "%s last-dim stride %lld != 1", name, (long long)v->stride[3]);
+    for (int i = 0; i < 3; ++i) {
+        if (v->stride[i] <= 0)
+            return fail(QKVX_ERR_LAYOUT, "%s.stride[%d] = %lld must be positive", name, i,
+                        (long long)v->stride[i]);
+        if (v->stride[i] % 8)
+            return fail(QKVX_ERR_ALIGNMENT,
+                        "%s.stride[%d] = %lld is not a multiple of 8 elements (16-byte rows)", name,
+                        i, (long long)v->stride[i]);
+    }
+    if (!aligned16(v->base))
+        return fail(QKVX_ERR_ALIGNMENT, "%s.base is not 16-byte aligned", name);
+    int64_t last = 0;
+    for (int i = 0; i < 4; ++i) last += (v->shape[i] - 1) * v->stride[i];
+    if (last + 1 >= kInt32Limit)
+        return fail(QKVX_ERR_INT32_RANGE, "%s spans %lld elements (limit 2^31)", name,
+                    (long long)(last + 1));
+    return QKVX_OK;
+}
+
+int ulysses_pack_qkv_head_chunk(const qkvx_view4* q, const qkvx_view4* k, const qkvx_view4* v,
+                                int world, const int* schedule, int n_chunks, int chunk,
+                                const qkvx_peers* dst, void* stream) {
+    const qkvx_view4* parts[3] = {q, k, v};
+    const char* names[3] = {"q", "k", "v"};
+    for (int i = 0; i < 3; ++i) {
+        int st = check_view(parts[i], names[i]);
+        if (st) return st;
+    }
+    for (int i = 1; i < 3; ++i)
+        for (int j = 0; j < 4; ++j)
+            if (parts[i]->shape[j] != q->shape[j])
+                return fail(QKVX_ERR_INVALID, "%s.shape differs from q.shape", names[i]);
+    if (world < 1 || world > QKVX_MAX_WORLD)
+        return fail(QKVX_ERR_INVALID, "world %d outside [1, %d]", world, QKVX_MAX_WORLD);
+    const int64_t B = q->shape[0], S = q->shape[1], H = q->shape[2];
+    if (H % world)
+        return fail(QKVX_ERR_DIVISIBILITY, "H = %lld is not divisible by world %d", (long long)H,
+                    world);
+    const int hl = int(H / world);
+    int off = 0, hc = 0;
+    int st = check_schedule(schedule, n_chunks, chunk, hl, &off, &hc);
+    if (st) return st;
+    st = check_peers(dst, "dst", world, B, S, hc, 3 * QKVX_HEAD_DIM);
+    if (st) return st;
+    const int64_t total = B * S * hc * 48;
+    if (total >= kInt32Limit)
+        return fail(QKVX_ERR_INT32_RANGE, "chunk payload of %lld vectors exceeds 2^31",
+                    (long long)total);
+    for (int u = 0; u < world; ++u) {
+        Range t = peers_touched(dst, u, B, S, hc, 3 * QKVX_HEAD_DIM);
+        for (int i = 0; i < 3; ++i)
+            if (overlap(t, view_range(parts[i]->base, parts[i]->shape, parts[i]->stride, 4)))
+                return fail(QKVX_ERR_ALIAS, "dst.base[%d] overlaps %s", u, names[i]);
+    }
+    PackArgs a;
+    memset(&a, 0, sizeof(a));
+    for (int i = 0; i < 3; ++i) {
+        a.src[i] = static_cast<const uint16_t*>(parts[i]->base) + int64_t(off) * parts[i]->stride[2];
+        a.sb[i] = parts[i]->stride[0];
+        a.ss[i] = parts[i]->stride[1];
+        a.sh[i] = parts[i]->stride[2];
+    }
+    a.db = dst->stride[0];
+    a.ds = dst->stride[1];
+    a.dh = dst->stride[2];
+    a.total = uint32_t(total);
+    a.local_heads = hl;
+    a.div_hc = FastDiv(uint32_t(hc));
+    a.div_s = FastDiv(uint32_t(S));
+    for (int u = 0; u < world; ++u)
+        a.dst[u] = static_cast<uint16_t*>(dst->base[u]) + dst->row_offset * dst->stride[1] +
+                   dst->head_offset * dst->stride[2];
+    hipError_t e = launch_pack(a, world, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "pack launch");
+    return ok();
+}
+
+int ulysses_merge_output_head_chunk(const qkvx_peers* src, int world, int local_heads,
+                                    const int* schedule, int n_chunks, int chunk, void* out,
+                                    int batch, int s_local, void* stream) {
+    if (!out) return fail(QKVX_ERR_INVALID, "out is NULL");
+    if (world < 1 || world > QKVX_MAX_WORLD)
+        return fail(QKVX_ERR_INVALID, "world %d outside [1, %d]", world, QKVX_MAX_WORLD);
+    if (local_heads < 1) return fail(QKVX_ERR_INVALID, "local_heads must be >= 1");
+    if (batch < 1 || s_local < 1)
+        return fail(QKVX_ERR_INVALID, "batch %d and s_local %d must be >= 1", batch, s_local);
+    if (!aligned16(out)) return fail(QKVX_ERR_ALIGNMENT, "out is not 16-byte aligned");
+    int off = 0, hc = 0;
+    int st = check_schedule(schedule, n_chunks, chunk, local_heads, &off, &hc);
+    if (st) return st;
+    st = check_peers(src, "src", world, batch, s_local, hc, QKVX_HEAD_DIM);
+    if (st) return st;
+    const int64_t H = int64_t(world) * local_heads;
+    const int64_t out_elems = int64_t(batch) * s_local * H * 128;
+    if (out_elems >= kInt32Limit)
+        return fail(QKVX_ERR_INT32_RANGE, "out spans %lld elements (limit 2^31)",
+                    (long long)out_elems);
+    const int64_t total = int64_t(batch) * s_local * hc * 16;
+    const Range orng = bytes_range(out, out_elems * 2);
+    for (int u = 0; u < world; ++u)
+        if (overlap(orng, peers_touched(src, u, batch, s_local, hc, QKVX_HEAD_DIM)))
+            return fail(QKVX_ERR_ALIAS, "src.base[%d] overlaps out", u);
+    MergeArgs a;
+    memset(&a, 0, sizeof(a));
+    a.out = static_cast<uint16_t*>(out) + int64_t(off) * 128;
+    a.ob = int64_t(s_local) * H * 128;
+    a.os = H * 128;
+    a.sb = src->stride[0];
+    a.ss = src->stride[1];
+    a.sh = src->stride[2];
+    a.total = uint32_t(total);
+    a.local_heads = local_heads;
+    a.div_hc = FastDiv(uint32_t(hc));
+    a.div_s = FastDiv(uint32_t(s_local));
+    for (int u = 0; u < world; ++u)
+        a.src[u] = static_cast<const uint16_t*>(src->base[u]) + src->row_offset * src->stride[1] +
+                   src->head_offset * src->stride[2];
+    hipError_t e = launch_merge(a, world, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "merge launch");
+    return ok();
+}
+
+}  // extern "C"

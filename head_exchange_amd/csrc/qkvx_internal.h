@@ -1,0 +1,103 @@
+// Internal declarations shared by the host library and the gfx950 kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "qkvx.h"
+
+namespace qkvx {
+
+// Unsigned 32-bit division by a runtime divisor through a multiply-high and a
+// shift (Granlund & Montgomery, "Division by invariant integers using
+// multiplication", PLDI 1994, the round-up variant):
+//   l = ceil(log2 d),  m = floor(2^32 * (2^l - d) / d) + 1,
+//   n / d = (mulhi(n, m) + n) >> l          for 0 <= n < 2^31, d >= 1.
+// Index arithmetic of the transport kernels is bounded below 2^31, so the
+// 33-bit intermediate never wraps.
+struct FastDiv {
+    uint32_t d;
+    uint32_t m;
+    uint32_t l;
+
+    __host__ __device__ FastDiv() : d(1), m(1), l(0) {}
+    __host__ explicit FastDiv(uint32_t divisor) : d(divisor) {
+        uint32_t ll = 0;
+        while ((uint64_t(1) << ll) < divisor) ++ll;
+        l = ll;
+        uint64_t mm = ((uint64_t(1) << 32) * ((uint64_t(1) << ll) - divisor)) / divisor + 1;
+        m = uint32_t(mm);
+    }
+    __host__ __device__ __forceinline__ uint32_t div(uint32_t n) const {
+#if defined(__HIP_DEVICE_COMPILE__)
+        uint32_t hi = __umulhi(n, m);
+#else
+        uint32_t hi = uint32_t((uint64_t(n) * m) >> 32);
+#endif
+        return (hi + n) >> l;
+    }
+    __host__ __device__ __forceinline__ void divmod(uint32_t n, uint32_t& q, uint32_t& r) const {
+        q = div(n);
+        r = n - q * d;
+    }
+};
+
+// ---------------------------------------------------------------------------
+// fused projection kernel arguments
+// ---------------------------------------------------------------------------
+struct FusedArgs {
+    const uint16_t* x;        // [M, K] bf16
+    const uint16_t* w;        // [N, K] bf16
+    const float* wq;          // [128]
+    const float* wk;          // [128]
+    const float* cs;          // [rows, 128]
+    uint16_t* slot;           // region (t, 0) of the call's slot
+    int64_t region_elems;     // elements between destination regions
+    int64_t part_stride;      // elements between q, k and v of one destination
+    int64_t stride_b, stride_s, stride_h;
+    int32_t M, N, K;
+    int32_t hidden;           // = K
+    int32_t local_heads;      // H_local
+    int32_t s_local;
+    int32_t row0;             // rank * s_local: first sequence row and position
+    int32_t tiles_m, tiles_n;
+    int32_t group_m;          // tile-row group of the tile order
+    float eps;
+};
+
+// ---------------------------------------------------------------------------
+// pack / merge kernel arguments
+// ---------------------------------------------------------------------------
+struct PackArgs {
+    const uint16_t* src[3];        // q, k, v at [0, 0, off, 0]
+    int64_t sb[3], ss[3], sh[3];   // their strides (b, s, h)
+    int64_t db, ds, dh;            // destination strides (b, row, head)
+    uint32_t total;                // 16-byte chunks per destination
+    int32_t local_heads;
+    FastDiv div_hc, div_s;
+    uint16_t* dst[QKVX_MAX_WORLD]; // peer d at [0, row_offset, head_offset, 0]
+};
+
+struct MergeArgs {
+    uint16_t* out;                 // [B, S, world*local_heads, 128] at head off
+    int64_t ob, os;                // out strides (b, s); head stride is 128
+    int64_t sb, ss, sh;            // source strides (b, row, head)
+    uint32_t total;                // 16-byte chunks per source
+    int32_t local_heads;
+    FastDiv div_hc, div_s;
+    const uint16_t* src[QKVX_MAX_WORLD];  // peer u at [0, row_offset, head_offset, 0]
+};
+
+// Launchers (enqueue only; arguments already validated).
+hipError_t launch_fused(const FusedArgs& a, hipStream_t stream);
+hipError_t launch_pack(const PackArgs& a, int world, hipStream_t stream);
+hipError_t launch_merge(const MergeArgs& a, int world, hipStream_t stream);
+hipError_t launch_fill16(uint16_t* p, int64_t n, uint16_t value, hipStream_t stream);
+
+// Tile plan of the fused kernel (exposed for describe()).
+struct FusedPlan {
+    int block_m, block_n, block_k, threads, group_m;
+};
+FusedPlan fused_plan();
+
+}  // namespace qkvx

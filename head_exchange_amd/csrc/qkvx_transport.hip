@@ -1,0 +1,119 @@
+// Head-chunk pack and merge kernels for gfx950.
+//
+// Both are bit copies between strided bf16 tensors whose innermost axis is one
+// 128-element (256-byte) head vector, so every access is a 16-byte vector and a
+// group of 16 lanes moves one whole head: a wave touches four 256-byte runs per
+// instruction on each side, i.e. whole 128-byte cache lines.  Reading the pages'
+// index maps ("Head-Chunk Layout and Transport Primitives" on
+// docs.flashinfer.ai/api/comm.html):
+//   pack : dst_d[b, R0 + s, j, p*128 + e] = part_p[b, s, d*H_local + off + j, e]
+//   merge: out[b, s, u*H_local + off + j, e] = src_u[b, R0 + s, j0 + j, e]
+// The peer index (d or u) is blockIdx.y, so the peer's base pointer is a
+// wave-uniform kernel argument and no per-lane table lookup is needed; the rest
+// of the flat 16-byte-chunk index is split with precomputed 32-bit dividers.
+#include "qkvx_internal.h"
+
+namespace qkvx {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kVec = 4;   // 16-byte chunks per thread: four loads in flight before the stores
+
+__global__ __launch_bounds__(kThreads) void pack_kernel(PackArgs a) {
+    const uint32_t d = blockIdx.y;
+    uint16_t* __restrict__ dst = a.dst[d];
+    const uint32_t first = blockIdx.x * (kThreads * kVec) + threadIdx.x;
+    uint4 val[kVec];
+    uint16_t* ptr[kVec];
+#pragma unroll
+    for (int i = 0; i < kVec; ++i) {
+        const uint32_t c = first + i * kThreads;
+        ptr[i] = nullptr;
+        if (c < a.total) {
+            const uint32_t e16 = c & 15u;
+            uint32_t u = c >> 4;
+            const uint32_t p = u % 3u;            // q, k, v interleaved per head
+            u = u / 3u;
+            uint32_t tok, j, b, s;
+            a.div_hc.divmod(u, tok, j);
+            a.div_s.divmod(tok, b, s);
+            const uint16_t* src = p == 0 ? a.src[0] : (p == 1 ? a.src[1] : a.src[2]);
+            const int64_t sb = p == 0 ? a.sb[0] : (p == 1 ? a.sb[1] : a.sb[2]);
+            const int64_t ss = p == 0 ? a.ss[0] : (p == 1 ? a.ss[1] : a.ss[2]);
+            const int64_t sh = p == 0 ? a.sh[0] : (p == 1 ? a.sh[1] : a.sh[2]);
+            src += b * sb + s * ss + int64_t(d * a.local_heads + j) * sh + e16 * 8;
+            val[i] = *reinterpret_cast<const uint4*>(src);
+            ptr[i] = dst + b * a.db + s * a.ds + j * a.dh + p * 128 + e16 * 8;
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < kVec; ++i)
+        if (ptr[i]) *reinterpret_cast<uint4*>(ptr[i]) = val[i];
+}
+
+__global__ __launch_bounds__(kThreads) void merge_kernel(MergeArgs a) {
+    const uint32_t u = blockIdx.y;
+    const uint16_t* __restrict__ src = a.src[u];
+    uint16_t* __restrict__ out = a.out + int64_t(u) * a.local_heads * 128;
+    const uint32_t first = blockIdx.x * (kThreads * kVec) + threadIdx.x;
+    uint4 val[kVec];
+    uint16_t* ptr[kVec];
+#pragma unroll
+    for (int i = 0; i < kVec; ++i) {
+        const uint32_t c = first + i * kThreads;
+        ptr[i] = nullptr;
+        if (c < a.total) {
+            const uint32_t e16 = c & 15u;
+            uint32_t tok, j, b, s;
+            a.div_hc.divmod(c >> 4, tok, j);
+            a.div_s.divmod(tok, b, s);
+            val[i] = *reinterpret_cast<const uint4*>(src + b * a.sb + s * a.ss + j * a.sh + e16 * 8);
+            ptr[i] = out + b * a.ob + s * a.os + j * 128 + e16 * 8;
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < kVec; ++i)
+        if (ptr[i]) *reinterpret_cast<uint4*>(ptr[i]) = val[i];
+}
+
+__global__ __launch_bounds__(kThreads) void fill16_kernel(uint16_t* p, int64_t n, uint32_t pattern) {
+    const int64_t nvec = n / 8;
+    const uint4 v = make_uint4(pattern, pattern, pattern, pattern);
+    const int64_t stride = int64_t(gridDim.x) * kThreads;
+    for (int64_t i = int64_t(blockIdx.x) * kThreads + threadIdx.x; i < nvec; i += stride)
+        reinterpret_cast<uint4*>(p)[i] = v;
+    // tail (fewer than 8 elements), written by the first lanes of block 0
+    if (blockIdx.x == 0 && threadIdx.x < n - nvec * 8)
+        p[nvec * 8 + threadIdx.x] = uint16_t(pattern);
+}
+
+}  // namespace
+
+hipError_t launch_pack(const PackArgs& a, int world, hipStream_t stream) {
+    if (a.total == 0) return hipSuccess;
+    const uint32_t per_block = kThreads * kVec;
+    dim3 grid((a.total + per_block - 1) / per_block, world);
+    hipLaunchKernelGGL(pack_kernel, grid, dim3(kThreads), 0, stream, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_merge(const MergeArgs& a, int world, hipStream_t stream) {
+    if (a.total == 0) return hipSuccess;
+    const uint32_t per_block = kThreads * kVec;
+    dim3 grid((a.total + per_block - 1) / per_block, world);
+    hipLaunchKernelGGL(merge_kernel, grid, dim3(kThreads), 0, stream, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_fill16(uint16_t* p, int64_t n, uint16_t value, hipStream_t stream) {
+    if (n <= 0) return hipSuccess;
+    const uint32_t pattern = uint32_t(value) | (uint32_t(value) << 16);
+    int64_t blocks = (n / 8 + kThreads - 1) / kThreads;
+    if (blocks < 1) blocks = 1;
+    if (blocks > 65536) blocks = 65536;
+    hipLaunchKernelGGL(fill16_kernel, dim3(uint32_t(blocks)), dim3(kThreads), 0, stream, p, n,
+                       pattern);
+    return hipGetLastError();
+}
+
+}  // namespace qkvx

@@ -1,0 +1,253 @@
+"""CPU checks of the C ABI: the library loads, exports every symbol the header
+declares, and its host-side validation rejects invalid calls with the right
+status before anything touches a GPU (only fake, never dereferenced device
+addresses are passed; no call here reaches a kernel launch)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import head_exchange_amd as hx
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "qkvx.h")
+FAKE = 1 << 40          # an aligned address that is never dereferenced here
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(hx.LIB_PATH):
+        from head_exchange_amd import build
+        build.build()
+    return hx.load()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return re.findall(r"QKVX_API\s+[\w\s\*]+?\b(\w+)\s*\(", text)
+
+
+def test_header_declares_the_entry_points():
+    names = set(declared_functions())
+    assert names == set(hx.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol(lib):
+    out = subprocess.run(["nm", "-D", "--defined-only", hx.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = {line.split()[-1] for line in out.splitlines() if " T " in line}
+    for name in declared_functions():
+        assert name in exported, name
+        assert getattr(lib, name) is not None
+    # nothing but the C ABI is exported
+    assert exported == set(declared_functions())
+
+
+def test_status_codes_match_header():
+    text = open(HEADER).read()
+    codes = dict((int(v), k) for k, v in re.findall(r"QKVX_(?:OK|ERR_(\w+))\s*=\s*(-?\d+)", text)
+                 if k) | {0: "OK"}
+    for code, name in hx.STATUS.items():
+        if code:
+            assert codes[code] == name
+
+
+def create(lib, hidden=512, heads=4, world=2, layout=0, max_tokens=64, slots=2,
+           mem=FAKE, nbytes=None):
+    h = ctypes.c_void_p()
+    if nbytes is None:
+        nbytes = lib.qkvx_slot_bytes(hidden, world, max_tokens, slots)
+    st = lib.qkvx_create(hidden, heads, 128, world, layout, max_tokens, slots,
+                         ctypes.c_void_p(mem), nbytes, ctypes.byref(h))
+    return st, h
+
+
+def test_slot_bytes(lib):
+    assert lib.qkvx_slot_bytes(7168, 4, 9472, 2) == 2 * 4 * 9472 * 3 * 7168 * 2
+    assert lib.qkvx_slot_bytes(0, 4, 9472, 2) == 0
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(heads=3), -1),                       # hidden != heads * 128
+    (dict(hidden=384, heads=3, world=2), -2),  # heads % world
+    (dict(world=0), -1),
+    (dict(world=65), -1),
+    (dict(layout=2), -7),
+    (dict(max_tokens=0), -1),
+    (dict(slots=0), -1),
+    (dict(nbytes=100), -3),                    # caller memory too small
+    (dict(mem=FAKE + 16), -4),                 # not 256-byte aligned
+    (dict(hidden=128 * 256, heads=256, max_tokens=1), -6),   # W_qkv >= 2^31 elements
+])
+def test_create_rejects(lib, kw, status):
+    st, h = create(lib, **kw)
+    assert st == status, lib.qkvx_last_error()
+    assert lib.qkvx_last_error()
+
+
+def test_create_and_describe_without_device(lib):
+    import json
+    st, h = create(lib)
+    assert st == 0
+    n = lib.qkvx_describe(h, None, 0)
+    buf = ctypes.create_string_buffer(n + 1)
+    lib.qkvx_describe(h, buf, n + 1)
+    d = json.loads(buf.value.decode())
+    assert d["local_heads"] == 2 and d["owns_slots"] is False and d["next_slot"] == 0
+    o = hx.Outputs()
+    assert lib.qkvx_last_outputs(h, ctypes.byref(o)) == -1
+    assert lib.qkvx_destroy(h) == 0
+
+
+def forward(lib, h, x=FAKE + (1 << 36), batch=1, s_local=32, w=FAKE + (2 << 36),
+            wq=FAKE + (3 << 36), wk=FAKE + (3 << 36) + 512, cs=FAKE + (4 << 36), rows=128,
+            rank=0):
+    return lib.qkvx_forward(h, ctypes.c_void_p(x), batch, s_local, ctypes.c_void_p(w),
+                            ctypes.c_void_p(wq), ctypes.c_void_p(wk), ctypes.c_void_p(cs), rows,
+                            rank, None, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(x=0), -1),
+    (dict(batch=0), -1),
+    (dict(batch=3, s_local=32), -3),           # 96 tokens > max_tokens 64
+    (dict(rank=2), -1),
+    (dict(rank=-1), -1),
+    (dict(rank=1, s_local=64, rows=100), -3),  # positions up to 128 needed
+    (dict(cs=FAKE + (4 << 36) + 8), -4),       # misaligned table
+    (dict(wq=FAKE + (3 << 36) + 4), -4),       # misaligned norm weight
+    (dict(x=FAKE + 2), -4),
+    (dict(x=FAKE + 4096), -5),                 # x inside the receive slots
+    (dict(cs=FAKE), -5),
+])
+def test_forward_rejects_before_launch(lib, kw, status):
+    st, h = create(lib)
+    assert st == 0
+    try:
+        assert forward(lib, h, **kw) == status, lib.qkvx_last_error()
+        # a rejected call does not advance the slot cycle
+        buf = ctypes.create_string_buffer(4096)
+        lib.qkvx_describe(h, buf, 4096)
+        assert b'"calls": 0' in buf.value
+    finally:
+        lib.qkvx_destroy(h)
+
+
+def view(base, shape, stride):
+    v = hx.View4()
+    v.base = base
+    for i in range(4):
+        v.shape[i] = shape[i]
+        v.stride[i] = stride[i]
+    return v
+
+
+def contiguous(shape):
+    st, acc = [], 1
+    for s in reversed(shape):
+        st.append(acc)
+        acc *= s
+    return list(reversed(st))
+
+
+def peers(bases, batch, rows, heads, inner, row_offset=0, head_offset=0, stride=None):
+    p = hx.Peers()
+    p.world = len(bases)
+    p.batch, p.rows, p.heads = batch, rows, heads
+    st = stride or contiguous([batch, rows, heads, inner])[:3]
+    for i in range(3):
+        p.stride[i] = st[i]
+    p.row_offset, p.head_offset = row_offset, head_offset
+    for u, b in enumerate(bases):
+        p.base[u] = b
+    return p
+
+
+def pack(lib, q, k, v, world, sched, chunk, dst):
+    arr = (ctypes.c_int * len(sched))(*sched)
+    return lib.ulysses_pack_qkv_head_chunk(ctypes.byref(q), ctypes.byref(k), ctypes.byref(v), world,
+                                           arr, len(sched), chunk, ctypes.byref(dst), None)
+
+
+QKV_SHAPE = [1, 64, 8, 128]
+QS = contiguous(QKV_SHAPE)
+SRC = [FAKE, FAKE + (1 << 30), FAKE + (2 << 30)]
+DST = [FAKE + (8 << 30) + d * (1 << 28) for d in range(2)]
+
+
+def good_pack_args():
+    q, k, v = (view(b, QKV_SHAPE, QS) for b in SRC)
+    dst = peers(DST, 1, 128, 4, 384, row_offset=64)
+    return q, k, v, dst
+
+
+@pytest.mark.parametrize("mutate,status", [
+    (lambda a: a.update(sched=[1, 2]), -2),                 # sums to 3, H_local is 4
+    (lambda a: a.update(sched=[4, 0]), -2),                 # zero count
+    (lambda a: a.update(chunk=2), -1),
+    (lambda a: a.update(world=3), -2),                      # 8 % 3
+    (lambda a: a["q"].shape.__setitem__(3, 64), -1),        # head_dim 64
+    (lambda a: a["k"].stride.__setitem__(3, 2), -7),        # inner stride
+    (lambda a: a["v"].stride.__setitem__(1, -1024), -7),    # negative stride
+    (lambda a: a["q"].stride.__setitem__(2, 132), -4),      # 264-byte head stride
+    (lambda a: setattr(a["q"], "base", FAKE + 8), -4),
+    (lambda a: setattr(a["dst"], "row_offset", 65), -3),    # rows 65..128 > 128
+    (lambda a: setattr(a["dst"], "heads", 1), -3),          # chunk of 2 heads does not fit
+    (lambda a: a["dst"].stride.__setitem__(2, 256), -7),    # heads of 384 would overlap
+    (lambda a: setattr(a["dst"], "world", 4), -1),
+    (lambda a: a["dst"].base.__setitem__(1, SRC[1] + 4096 - 64 * 1536 * 2), -5),  # rows land in k
+    (lambda a: a["dst"].base.__setitem__(0, 0), -1),
+])
+def test_pack_rejects(lib, mutate, status):
+    q, k, v, dst = good_pack_args()
+    a = dict(q=q, k=k, v=v, dst=dst, world=2, sched=[2, 2], chunk=0)
+    mutate(a)
+    st = pack(lib, a["q"], a["k"], a["v"], a["world"], a["sched"], a["chunk"], a["dst"])
+    assert st == status, lib.qkvx_last_error()
+
+
+def test_pack_rejects_int32_overflow(lib):
+    shape = [1, 1 << 20, 64, 128]                # 2^33 elements
+    q = view(SRC[0], shape, contiguous(shape))
+    dst = peers(DST, 1, 1 << 21, 32, 384)
+    assert pack(lib, q, q, q, 2, [32], 0, dst) == -6
+
+
+def merge(lib, src, world, local_heads, sched, chunk, out, batch, s_local):
+    arr = (ctypes.c_int * len(sched))(*sched)
+    return lib.ulysses_merge_output_head_chunk(ctypes.byref(src), world, local_heads, arr,
+                                               len(sched), chunk, ctypes.c_void_p(out), batch,
+                                               s_local, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(), None),
+    (dict(sched=[3, 3, 3]), -2),
+    (dict(out=FAKE + 2), -4),
+    (dict(out=0), -1),
+    (dict(local_heads=0), -1),
+    (dict(s_local=1000), -3),                  # source rows too few
+    (dict(out=DST[0]), -5),
+])
+def test_merge_rejects(lib, kw, status):
+    args = dict(world=2, local_heads=14, sched=[2, 10, 2], chunk=1, out=FAKE + (9 << 30),
+                batch=1, s_local=64)
+    args.update(kw)
+    src = peers(DST, 1, 128, 14, 128)
+    if status is None:
+        return        # the valid call would launch; it is exercised on the GPU
+    assert merge(lib, src, **args) == status, lib.qkvx_last_error()
+
+
+def test_python_binding_fails_loudly_without_library(tmp_path):
+    import importlib
+    mod = importlib.reload(hx)
+    saved = mod._lib
+    try:
+        mod._lib = None
+        with pytest.raises(ImportError):
+            mod.load(str(tmp_path / "missing.so"))
+    finally:
+        mod._lib = saved

@@ -1,0 +1,217 @@
+"""GPU parity of the fused QKV projection + RMSNorm + RoPE + head-band store.
+
+Every case compares the receive slots written by the HIP kernel (through the
+C ABI) with the CPU oracle on the same seeded inputs, under the acceptance rule
+of ``helpers.check_fp``.  Small shapes are compared element by element over
+whole slots (several tiles, ragged M and N tails, both layouts, U = 1, odd
+head counts); the five full-size workloads, in the launch configuration the
+benchmark times, are compared on sampled tokens (all heads, all destinations),
+and on the coverage property over the whole slot.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+import workloads as W
+from helpers import check_fp, f32_dev, slot_full, slot_rows, to_bits, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+class Inputs:
+    """Seeded inputs of one workload, on the host and on the device."""
+
+    def __init__(self, wl: W.Workload, call: int = 0, x_bits=None, w_bits=None):
+        self.wl = wl
+        self.x = W.x_input(wl, call) if x_bits is None else x_bits
+        self.w = W.w_qkv(wl) if w_bits is None else w_bits
+        self.wq, self.wk = W.norm_weights(wl)
+        self.cs = W.table(wl)
+        self.dx = to_dev(self.x)
+        self.dw = to_dev(self.w)
+        self.dwq, self.dwk, self.dcs = f32_dev(self.wq), f32_dev(self.wk), f32_dev(self.cs)
+
+
+def make_session(hx, wl: W.Workload, max_tokens=None, num_slots=None):
+    return hx.qkvx_create(wl.hidden, wl.heads, 128, wl.world, wl.layout,
+                          max_tokens or wl.tokens, num_slots or wl.num_slots)
+
+
+def run(sess, inp: Inputs, rank=None):
+    return sess.forward(inp.dx, inp.dw, inp.dwq, inp.dwk, inp.dcs,
+                        inp.wl.rank if rank is None else rank)
+
+
+def oracle_rows(inp: Inputs, tokens: np.ndarray, rank: int) -> np.ndarray:
+    """Oracle float64 [T, 3, H, 128] for flat token indices of the shard."""
+    wl = inp.wl
+    x2 = inp.x.reshape(wl.tokens, wl.hidden)
+    s = tokens % wl.s_local
+    pos = rank * wl.s_local + s
+    return O.front_end_rows(x2[tokens], inp.w, inp.wq, inp.wk, inp.cs[pos], wl.heads)
+
+
+def sample_tokens(wl: W.Workload, n: int = 48, seed: int = 0) -> np.ndarray:
+    """First/last tokens, tile edges, batch edges and random ones."""
+    M = wl.tokens
+    cand = {0, 1, M - 1, M - 2, wl.s_local - 1, min(wl.s_local, M - 1)}
+    for edge in range(256, M, 256 * max(1, M // 2048)):
+        cand.update({edge - 1, edge})
+    rng = np.random.default_rng(seed)
+    cand.update(rng.integers(0, M, n).tolist())
+    return np.array(sorted(c for c in cand if 0 <= c < M))
+
+
+def check_sampled(views, inp: Inputs, rank: int, tokens: np.ndarray, label: str):
+    wl = inp.wl
+    got = slot_rows(views, wl.layout, tokens // wl.s_local, rank * wl.s_local + tokens % wl.s_local)
+    ref = oracle_rows(inp, tokens, rank)
+    for p, name in enumerate("qkv"):
+        check_fp(got[:, p], ref[:, p], f"{label}:{name}")
+
+
+def check_full(views, inp: Inputs, rank: int, label: str, poison=True):
+    """Whole slots: this rank's rows match the oracle, every other row still
+    holds the poison pattern."""
+    wl = inp.wl
+    vals = O.front_end_values(inp.x, inp.w, inp.wq, inp.wk, inp.cs, wl.heads, rank)
+    got = slot_full(views, wl.layout)
+    r0, r1 = rank * wl.s_local, (rank + 1) * wl.s_local
+    hl = wl.local_heads
+    for d in range(wl.world):
+        g = got[d]                                          # [3, B, S_g, hl, 128]
+        ref = np.moveaxis(vals[:, :, :, d * hl:(d + 1) * hl], 2, 0)
+        for p, name in enumerate("qkv"):
+            check_fp(g[p][:, r0:r1], ref[p], f"{label}:d{d}:{name}")
+        if poison:
+            assert np.all(g[:, :, :r0] == O.POISON_BITS), f"{label}: rows before rank {rank} written"
+            assert np.all(g[:, :, r1:] == O.POISON_BITS), f"{label}: rows after rank {rank} written"
+
+
+SMALL = [
+    # several tiles in M and N, ragged M (400 = 256 + 144), bshd, rank 1 of 2
+    W.custom(11, batch=2, s_local=200, heads=8, world=2, rank=1, layout="bshd",
+             schedule=(1, 3), rope_base=1e4),
+    # fused layout, U = 4, ragged M (300 tokens), rank 3
+    W.custom(12, batch=1, s_local=300, heads=8, world=4, rank=3, layout="fused",
+             schedule=(2,), rope_base=1e6),
+    # odd head count: N = 3 * 3 * 128 = 1152 is not a multiple of the 256-wide tile
+    W.custom(13, batch=1, s_local=70, heads=3, world=3, rank=1, layout="bshd",
+             schedule=(1,), rope_base=1e4),
+    # U = 1: the slot is the whole [B, S, H, .] output (identity placement)
+    W.custom(14, batch=3, s_local=40, heads=4, world=1, rank=0, layout="fused",
+             schedule=(4,), rope_base=1e4),
+    # M < one tile; a single token per batch entry
+    W.custom(15, batch=5, s_local=1, heads=2, world=2, rank=1, layout="bshd",
+             schedule=(1,), rope_base=1e4),
+]
+
+
+@pytest.mark.parametrize("wl", SMALL, ids=lambda w: w.name)
+def test_small_full_slots(gpu_lib, wl):
+    inp = Inputs(wl)
+    sess = make_session(gpu_lib, wl)
+    sess.poison_receive_slots()
+    views = run(sess, inp)
+    torch.cuda.synchronize()
+    check_full(views, inp, wl.rank, wl.name)
+
+
+def test_tiny_workload_full(gpu_lib):
+    wl = W.WORKLOADS["tiny"]
+    inp = Inputs(wl)
+    sess = make_session(gpu_lib, wl)
+    sess.poison_receive_slots()
+    views = run(sess, inp)
+    torch.cuda.synchronize()
+    check_full(views, inp, wl.rank, wl.name)
+
+
+def test_all_ranks_simulate_the_exchange(gpu_lib):
+    """Every rank of a group of 4 runs on its shard of one global activation into
+    the same slots: slot d then holds heads [d*H_l, (d+1)*H_l) of every token of
+    the whole sequence, at global positions (scatter_heads of the full result)."""
+    world, s_local, heads, batch = 4, 96, 8, 2
+    wl = W.custom(16, batch=batch, s_local=s_local, heads=heads, world=world, rank=0,
+                  layout="bshd", schedule=(2,), rope_base=1e4)
+    gl = W.custom(17, batch=batch, s_local=world * s_local, heads=heads, world=1, rank=0,
+                  layout="bshd", schedule=(heads,), rope_base=1e4,
+                  cos_sin_rows=world * s_local)
+    xg = W.x_input(gl)
+    w = W.w_qkv(wl)
+    sess = make_session(gpu_lib, wl, num_slots=1)
+    sess.poison_receive_slots()
+    for r in range(world):
+        inp = Inputs(wl, x_bits=np.ascontiguousarray(xg[:, r * s_local:(r + 1) * s_local]), w_bits=w)
+        views = run(sess, inp, rank=r)
+    torch.cuda.synchronize()
+    wq, wk = W.norm_weights(wl)
+    full = O.front_end_values(xg, w, wq, wk, W.table(wl), heads, 0)   # [B, S_g, 3, H, 128]
+    got = slot_full(views, "bshd")
+    hl = heads // world
+    for d in range(world):
+        for p in range(3):
+            check_fp(got[d][p], full[:, :, p, d * hl:(d + 1) * hl], f"allranks:d{d}:{'qkv'[p]}")
+
+
+@pytest.mark.parametrize("name", ["h32_u4_fused", "h56_u4", "h56_u2_fused"])
+def test_full_size_sampled(gpu_lib, name):
+    wl = W.WORKLOADS[name]
+    inp = Inputs(wl)
+    sess = make_session(gpu_lib, wl)
+    sess.poison_receive_slots()
+    views = run(sess, inp)
+    torch.cuda.synchronize()
+    check_sampled(views, inp, wl.rank, sample_tokens(wl), name)
+    # coverage over the whole slot: own rows finite, other rows untouched poison
+    r0, r1 = wl.rank * wl.s_local, (wl.rank + 1) * wl.s_local
+    for v in views:
+        parts = v if wl.layout == "bshd" else (v,)
+        for t in parts:
+            bits = t.view(torch.int16)
+            own = bits[:, r0:r1]
+            assert not bool((own == int(O.POISON_BITS)).any()), f"{name}: unwritten element"
+            assert torch.isfinite(t[:, r0:r1]).all(), f"{name}: non-finite output"
+            if r0 > 0:
+                assert bool((bits[:, :r0] == int(O.POISON_BITS)).all())
+            if r1 < bits.shape[1]:
+                assert bool((bits[:, r1:] == int(O.POISON_BITS)).all())
+
+
+def test_stress_slot_cycling(gpu_lib):
+    """Four calls with fresh activations into two cycled slots: call i's views
+    are correct after call i+1 and are overwritten by call i+2."""
+    wl = W.WORKLOADS["h48_u8_stress"]
+    w = W.w_qkv(wl)
+    sess = make_session(gpu_lib, wl)
+    tokens = sample_tokens(wl, n=24)
+    history = []
+    for call in range(wl.calls):
+        inp = Inputs(wl, call=call, w_bits=w)
+        views = run(sess, inp)
+        assert sess.outputs_struct().slot == call % wl.num_slots
+        torch.cuda.synchronize()
+        check_sampled(views, inp, wl.rank, tokens, f"stress:call{call}")
+        if history:
+            pviews, pinp = history[-1]
+            check_sampled(pviews, pinp, wl.rank, tokens, f"stress:call{call - 1}-kept")
+        if call >= 2:
+            # the slot of call - 2 is reused by this call
+            assert views[0][0].data_ptr() == history[-2][0][0][0].data_ptr()
+        history.append((views, inp))
+
+
+def test_describe_and_last_outputs(gpu_lib):
+    import json
+    wl = W.WORKLOADS["tiny"]
+    sess = make_session(gpu_lib, wl)
+    d = json.loads(sess.describe())
+    assert d["world"] == 2 and d["local_heads"] == 2 and d["layout"] == "bshd"
+    assert d["next_slot"] == 0
+    inp = Inputs(wl)
+    views = run(sess, inp)
+    last = sess.last_outputs()
+    assert last[1][2].data_ptr() == views[1][2].data_ptr()
+    assert json.loads(sess.describe())["next_slot"] == 1
+    sess.close()
