@@ -1,0 +1,262 @@
+#!/usr/bin/env python3
+"""Benchmark of the per-GPU Ulysses attention front end on one MI355X.
+
+A step is one pass of the whole hot path over one batch of synthetic input of
+the 56-head, Ulysses-4 shard (B=1, S_local=9472, H=56, hidden=7168, bshd,
+schedule [2, 10, 2]):
+  * qkvx_forward: fused QKV projection + RMSNorm(Q, K) + RoPE + head-band store
+    into the 4 receive slots (host validation and planning included);
+  * ulysses_pack_qkv_head_chunk for every chunk of the schedule, into the 4
+    receive slots at rows rank*S_local..;
+  * ulysses_merge_output_head_chunk for every chunk, from a seeded attention
+    output band [1, 37888, 14, 128] into [1, 9472, 56, 128].
+Inputs are resident in HBM before the timed region.  ``value`` is the step's
+algorithmic projection FLOPs (2*M*N*K) over the step time; per-kernel times
+come from HIP events recorded on the launch stream inside the timed region.
+
+Prints one JSON line.  Only --gpus 1 is supported (one GPU's share of the
+exchange; the peers are simulated in local HBM).
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+WORKLOAD = "h56_u4"
+PEAK_BF16_TFLOPS = 2500.0       # MI355X dense bf16 MFMA
+PEAK_HBM_GBPS = 8000.0          # MI355X HBM3E
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fused_qkvx_h56_u4_traffic.txt")
+FUSED_SOURCE = os.path.join(ROOT, "head_exchange_amd", "csrc", "qkvx_fused.hip")
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--skip-cpu-baseline", action="store_true",
+                   help="do not time the CPU oracle (for profiler runs)")
+    p.add_argument("--cpu-seconds", type=float, default=12.0,
+                   help="target duration of the CPU oracle sample")
+    p.add_argument("--copy-calibration", action="store_true",
+                   help="also run a plain 1 GiB device copy (counter calibration)")
+    return p.parse_args()
+
+
+def source_hash(path: str) -> str:
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def read_traffic():
+    """HBM bytes per launch of the fused kernel from the committed counter
+    summary, or None when it is missing or the kernel changed since."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    kv = {}
+    for line in open(TRAFFIC_FILE):
+        if ":" in line and not line.startswith("#"):
+            k, v = line.split(":", 1)
+            kv[k.strip()] = v.strip()
+    if kv.get("kernel_source_sha256_16") != source_hash(FUSED_SOURCE):
+        return None
+    try:
+        return float(kv["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def cpu_baseline(wl, x, w, wq, wk, cs, qkv_src, band, target_s: float):
+    """The oracle, as it is, on a bounded sample of the same step: the first T
+    tokens of the shard through projection + norm + RoPE + rounding + placement,
+    and the pack and merge index maps of those T tokens for every chunk."""
+    import oracle as O
+    import workloads as W
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()
+                       if i.get("user_api") == "blas"] or [1])
+    except Exception:
+        threads = os.cpu_count() or 1
+    M, N, K = wl.gemm_shape
+    S, U, hl = wl.s_local, wl.world, wl.local_heads
+    sched = W.schedule_pairs(wl.schedule)
+
+    def step(T):
+        t0 = time.perf_counter()
+        xs = x[:, :T]
+        vals = O.front_end_values(xs, w, wq, wk, cs, wl.heads, wl.rank)
+        O.receive_slots(vals, U, wl.rank)
+        q, k, v = (a[:, :T] for a in qkv_src)
+        for off, cnt in sched:
+            dests = [np.empty((wl.batch, T, cnt, 384), np.uint16) for _ in range(U)]
+            O.pack_qkv_head_chunk_into(q, k, v, U, off, cnt, dests, 0)
+        out = np.empty((wl.batch, T, wl.heads, 128), np.uint16)
+        srcs = [band[:, u * S:u * S + T] for u in range(U)]
+        for off, cnt in sched:
+            O.merge_output_head_chunk(srcs, 0, off, U, hl, off, cnt, out)
+        return time.perf_counter() - t0
+
+    step(64)                                     # warm-up (allocations, BLAS threads)
+    t_a, t_b = step(64), step(256)
+    per_token = max((t_b - t_a) / 192.0, 1e-6)
+    fixed = max(t_a - 64 * per_token, 0.0)
+    T = int(min(S, max(256, (target_s - fixed) / per_token)))
+    T = max(64, (T // 64) * 64)
+    dt = step(T)
+    flops = 2.0 * wl.batch * T * N * K
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"first {T} of {S} tokens of the shard: float64 projection, RMSNorm, RoPE, "
+                      f"bf16 rounding and receive-slot placement, plus the pack and merge index "
+                      f"maps of those tokens for all {len(sched)} chunks; {dt:.1f} s wall",
+            "seconds": round(dt, 2), "tokens": T}
+
+
+def main():
+    args = parse()
+    world_env = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world_env != 1:
+        print(json.dumps({"error": "this benchmark measures one GPU's share of the Ulysses "
+                                   "exchange (peers simulated in local HBM); run it with --gpus 1"}))
+        sys.exit(2)
+
+    import torch
+    import workloads as W
+    import head_exchange_amd as hx
+
+    hx.load()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    wl = W.WORKLOADS[WORKLOAD]
+    M, N, K = wl.gemm_shape
+    S, U, hl, B = wl.s_local, wl.world, wl.local_heads, wl.batch
+    sched = W.schedule_pairs(wl.schedule)
+
+    def up(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(dev).view(torch.bfloat16)
+
+    # ---- seeded inputs, resident in HBM ------------------------------------
+    x_h = W.x_input(wl)
+    w_h = W.w_qkv(wl)
+    wq_h, wk_h = W.norm_weights(wl)
+    cs_h = W.table(wl)
+    qkv_h = W.pack_sources(wl)
+    band_h = W.merge_band(wl)
+    x, w = up(x_h), up(w_h)
+    wq, wk = torch.from_numpy(wq_h).to(dev), torch.from_numpy(wk_h).to(dev)
+    cs = torch.from_numpy(cs_h).to(dev)
+    q, k, v = (up(a) for a in qkv_h)
+    band = up(band_h)
+    sess = hx.qkvx_create(wl.hidden, wl.heads, 128, U, wl.layout, M, wl.num_slots)
+    pack_dst = [[torch.empty(B, wl.s_global, cnt, 384, dtype=torch.bfloat16, device=dev)
+                 for _ in range(U)] for _, cnt in sched]
+    merge_out = torch.empty(B, S, wl.heads, 128, dtype=torch.bfloat16, device=dev)
+    merge_src = [band[:, u * S:(u + 1) * S] for u in range(U)]
+    stream = torch.cuda.current_stream()
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        sess.forward(x, w, wq, wk, cs, wl.rank, stream)
+        if ev is not None:
+            ev[1].record(stream)
+        for c in range(len(sched)):
+            hx.ulysses_pack_qkv_head_chunk(q, k, v, world=U, schedule=wl.schedule, chunk=c,
+                                           dst=pack_dst[c], row_offset=wl.rank * S, stream=stream)
+        if ev is not None:
+            ev[2].record(stream)
+        for c, (off, _) in enumerate(sched):
+            hx.ulysses_merge_output_head_chunk(merge_src, world=U, local_heads=hl,
+                                               schedule=wl.schedule, chunk=c, out=merge_out,
+                                               head_offset=off, stream=stream)
+        if ev is not None:
+            ev[3].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(events[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    fused_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in events]))
+    pack_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in events]))
+    merge_ms = float(np.mean([e[2].elapsed_time(e[3]) for e in events]))
+    step_ms = wall * 1e3 / args.steps
+    flops = 2.0 * M * N * K
+    pack_bytes = sum(2.0 * B * S * U * cnt * 384 * 2 for _, cnt in sched)
+    merge_bytes = sum(2.0 * B * S * U * cnt * 128 * 2 for _, cnt in sched)
+    achieved = flops / (fused_ms * 1e-3) / 1e12
+    traffic = read_traffic()
+
+    calib = None
+    if args.copy_calibration:
+        src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        dst.copy_(src)
+        e1.record()
+        torch.cuda.synchronize()
+        calib = {"bytes": 2 * (1 << 30), "gbps": 2 * (1 << 30) / (e0.elapsed_time(e1) * 1e-3) / 1e9}
+        del src, dst
+
+    result = {
+        "metric": "fused QKV+norm+RoPE+pack TFLOP/s and head-band pack/merge GB/s, 1 GPU",
+        "value": flops / (step_ms * 1e-3) / 1e12,
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": step_ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": WORKLOAD, "batch": B, "s_local": S, "s_global": wl.s_global,
+                   "heads": wl.heads, "head_dim": 128, "hidden": wl.hidden, "world": U,
+                   "rank": wl.rank, "layout": wl.layout, "schedule": list(wl.schedule),
+                   "gemm_mnk": [M, N, K], "rope": "rotate_half", "rope_base": wl.rope_base,
+                   "parallelism": "ulysses shard of 4 (peers simulated in local HBM)"},
+        "roofline": {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS,
+                     "traffic": traffic, "kernel": "fused_qkv_kernel",
+                     "per_launch": f"2*M*N*K = {flops:.4g} FLOP"},
+        "transport": {"pack_us": pack_ms * 1e3, "pack_gbps": pack_bytes / (pack_ms * 1e-3) / 1e9,
+                      "pack_frac": pack_bytes / (pack_ms * 1e-3) / 1e9 / PEAK_HBM_GBPS,
+                      "merge_us": merge_ms * 1e3,
+                      "merge_gbps": merge_bytes / (merge_ms * 1e-3) / 1e9,
+                      "merge_frac": merge_bytes / (merge_ms * 1e-3) / 1e9 / PEAK_HBM_GBPS,
+                      "pack_bytes": pack_bytes, "merge_bytes": merge_bytes,
+                      "peak_gbps": PEAK_HBM_GBPS},
+        "kernels_ms": {"fused": fused_ms, "pack_all_chunks": pack_ms, "merge_all_chunks": merge_ms},
+    }
+    if calib:
+        result["copy_calibration"] = calib
+    if not args.skip_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(wl, x_h, w_h, wq_h, wk_h, cs_h, qkv_h, band_h,
+                                              args.cpu_seconds)
+    else:
+        result["cpu_baseline"] = None
+    sess.close()
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()
