@@ -35,23 +35,36 @@ namespace {
 
 constexpr int BM = 256;        // tokens per tile
 constexpr int BN = 256;        // output columns per tile (two heads)
-constexpr int BK = 64;         // K per pipeline stage
+constexpr int BK = 64;         // K per LDS stage (128 bytes of each operand row)
 constexpr int NT = 256;        // threads: four waves
 constexpr int GROUP_M = 8;     // tile rows walked together in the tile order
 constexpr int NXCD = 8;
 constexpr int CHUNKS = BK / 8;                 // 16-byte chunks per operand row
-constexpr int TILE_CHUNKS = BM * CHUNKS;       // 2048 chunks per operand tile
-constexpr int LOADS = TILE_CHUNKS / NT;        // 8 chunk loads per thread per operand
+// LDS image of one operand stage: 32 blocks of 8 rows x 128 bytes, each block
+// followed by 16 bytes of padding (65 chunks per block).
+constexpr int BLOCK_CHUNKS = 65;
+constexpr int STAGE_CHUNKS = 32 * BLOCK_CHUNKS;   // 2080 chunks = 33280 bytes
+constexpr int LOADS = 32 / 4;                  // block loads per wave per operand per stage
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
-// Chunk position of chunk c of tile row r.  Rows are 128 bytes, so eight rows
-// span 1 KB; the XOR pattern (r mod 8) ^ bit 3 of r gives every row of an
-// aligned group of 8 a different 16-byte slot, and does the same for the even
-// and for the odd rows of a group of 16.
-__device__ __forceinline__ int swz(int r) { return (r & 7) ^ ((r >> 3) & 1); }
+// LDS chunk index of chunk c of tile row r of one operand stage: block r / 8
+// holds rows 8 (r / 8) .. + 7 as 128 contiguous bytes each, and every 1 KB block
+// is followed by 16 bytes of padding.  A direct load (64 lanes x 16 bytes into
+// 1 KB of LDS) therefore reads eight consecutive rows' 128-byte segments in
+// ascending order -- one 128-byte request each.
+__device__ __forceinline__ int lds_chunk(int r, int c) {
+    return (r >> 3) * BLOCK_CHUNKS + (r & 7) * CHUNKS + c;
+}
+
+// Row of a 128-row wave range that MFMA row i (0..31) of 32-row block nb maps
+// to.  Lanes i..i+7 read the same chunk of rows 8 apart, i.e. of eight
+// consecutive blocks 1040 bytes apart: distinct LDS banks (32 and 64 banks).
+__device__ __forceinline__ int mfma_row(int nb, int i) {
+    return 64 * (nb >> 1) + 8 * (i & 7) + 4 * (nb & 1) + (i >> 3);
+}
 
 __device__ __forceinline__ void tile_coords(int bid, int tiles_m, int tiles_n, int group_m,
                                             int& tm, int& tn) {
@@ -79,12 +92,14 @@ __device__ __forceinline__ uint16_t bf16_bits(float f) {
 
 __global__ __attribute__((amdgpu_flat_work_group_size(NT, NT), amdgpu_waves_per_eu(1, 1)))
 void fused_qkv_kernel(FusedArgs a) {
-    __shared__ uint4 lds_w[2 * TILE_CHUNKS];   // 2 x 32 KB
-    __shared__ uint4 lds_x[2 * TILE_CHUNKS];   // 2 x 32 KB
+    // Two LDS stages per operand, as separate objects so that the compiler can
+    // tell a direct load into one stage from fragment reads of the other.
+    __shared__ uint4 lw0[STAGE_CHUNKS], lw1[STAGE_CHUNKS];   // 33280 bytes each
+    __shared__ uint4 lx0[STAGE_CHUNKS], lx1[STAGE_CHUNKS];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = tid >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
     const int wn = wave & 1;      // which head of the tile
     const int wm = wave >> 1;     // which 128 tokens of the tile
 
@@ -94,28 +109,29 @@ void fused_qkv_kernel(FusedArgs a) {
     const int n0 = tn * BN;
     const int K = a.K;
 
-    // ---- global -> LDS assignment: chunk (row = i*32 + tid/8, c = tid%8) ----
-    const int lrow = tid >> 3;
-    const int lc = tid & 7;
-    const int wslot = lrow * CHUNKS + (lc ^ swz(lrow));    // + i * 32 * CHUNKS
-    // byte sizes are below 2^32 (checked on the host); reads past them return 0
+    // ---- global -> LDS: direct loads (buffer_load ... lds) ----------------------
+    // Instruction i of wave w fills block b = 4 i + w of a stage: lane L brings
+    // chunk L % 8 of tile row 8 b + L / 8 to LDS offset 16 L of the block.
     const __amdgpu_buffer_rsrc_t rw = __builtin_amdgcn_make_buffer_rsrc(
         (void*)a.w, (short)0, int(uint32_t(a.N) * uint32_t(K) * 2u), 0x00020000);
     const __amdgpu_buffer_rsrc_t rx = __builtin_amdgcn_make_buffer_rsrc(
         (void*)a.x, (short)0, int(uint32_t(a.M) * uint32_t(K) * 2u), 0x00020000);
-    // byte offsets of this thread's first chunk of the W and X panels
-    const uint32_t gw0 = uint32_t(n0 + lrow) * uint32_t(K) * 2u + uint32_t(lc) * 16u;
-    const uint32_t gx0 = uint32_t(m0 + lrow) * uint32_t(K) * 2u + uint32_t(lc) * 16u;
-    const uint32_t row32 = 32u * uint32_t(K) * 2u;         // 32 rows further
+    // byte sizes are below 2^32 (checked on the host); reads past them return 0
+    const uint32_t rowbytes = uint32_t(K) * 2u;
+    const int wv = wave;
+    const uint32_t lrow = uint32_t(8 * wv + (lane >> 3));
+    const uint32_t gw0 = (uint32_t(n0) + lrow) * rowbytes + uint32_t(lane & 7) * 16u;
+    const uint32_t gx0 = (uint32_t(m0) + lrow) * rowbytes + uint32_t(lane & 7) * 16u;
 
-    // ---- fragment reads: lane owns row (lane%32) of each 32-row block --------
+    // ---- fragment reads: lane i%32 owns MFMA row i%32 of each 32-row block ----
     const int fr = lane & 31;
     const int hf = lane >> 5;
-    int koff[4];                                            // chunk slot per K-sub-step
+    int woff[4], xoff[4];                                   // chunk index of row, chunk hf
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) koff[ks] = fr * CHUNKS + ((2 * ks + hf) ^ swz(fr));
-    const int wbase = wn * 128 * CHUNKS;
-    const int xbase = wm * 128 * CHUNKS;
+    for (int b = 0; b < 4; ++b) {
+        woff[b] = lds_chunk(wn * 128 + mfma_row(b, fr), hf);
+        xoff[b] = lds_chunk(wm * 128 + mfma_row(b, fr), hf);
+    }
 
     f32x16 acc[4][4];
 #pragma unroll
@@ -125,57 +141,104 @@ void fused_qkv_kernel(FusedArgs a) {
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-    uint4 sw[LOADS], sx[LOADS];
-    auto load_tile = [&](int kt) {
+    // Request K-tile kt into stage s: 2 x LOADS block loads per wave.
+    auto load_stage = [&](int kt, int s) {
         const uint32_t kb = uint32_t(kt) * BK * 2u;
+        typedef __attribute__((address_space(3))) uint4 lds_uint4;
+        lds_uint4* dw = (lds_uint4*)((s ? lw1 : lw0) + wv * BLOCK_CHUNKS);
+        lds_uint4* dx = (lds_uint4*)((s ? lx1 : lx0) + wv * BLOCK_CHUNKS);
 #pragma unroll
         for (int i = 0; i < LOADS; ++i) {
-            sw[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
-                rw, gw0 + i * row32 + kb, 0, 0));
-            sx[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
-                rx, gx0 + i * row32 + kb, 0, 0));
-        }
-    };
-    auto store_tile = [&](int buf) {
-        uint4* lw = lds_w + buf * TILE_CHUNKS;
-        uint4* lx = lds_x + buf * TILE_CHUNKS;
-#pragma unroll
-        for (int i = 0; i < LOADS; ++i) {
-            lw[wslot + i * 32 * CHUNKS] = sw[i];
-            lx[wslot + i * 32 * CHUNKS] = sx[i];
+            const uint32_t roff = uint32_t(32 * i) * rowbytes + kb;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                rw, (__attribute__((address_space(3))) void*)(dw + 4 * i * BLOCK_CHUNKS), 16,
+                gw0 + roff, 0, 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                rx, (__attribute__((address_space(3))) void*)(dx + 4 * i * BLOCK_CHUNKS), 16,
+                gx0 + roff, 0, 0, 0);
         }
     };
 
-    const int KT = K / BK;
-    load_tile(0);
-    store_tile(0);
-    __syncthreads();
+    // Fragments of one 16-K sub-step: four 32-row blocks of W (A operand) and of
+    // X (B operand); sub-step ks reads chunks 2 ks + hf.  Two sets, A and B.
+    bf16x8 fa_a[4], fb_a[4], fa_b[4], fb_b[4];
+    auto read_frags = [&](int s, int ks, bf16x8* fa, bf16x8* fb) {
+        const uint4* w = s ? lw1 : lw0;
+        const uint4* x = s ? lx1 : lx0;
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+            fa[b] = __builtin_bit_cast(bf16x8, w[woff[b] + 2 * ks]);
+            fb[b] = __builtin_bit_cast(bf16x8, x[xoff[b] + 2 * ks]);
+        }
+    };
+    auto mfmas = [&](const bf16x8* fa, const bf16x8* fb) {
+#pragma unroll
+        for (int nb = 0; nb < 4; ++nb)
+#pragma unroll
+            for (int mb = 0; mb < 4; ++mb)
+                acc[nb][mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[nb], fb[mb], acc[nb][mb],
+                                                                     0, 0, 0);
+    };
 
-    for (int kt = 0; kt < KT; ++kt) {
-        const int cur = kt & 1;
-        if (kt + 1 < KT) load_tile(kt + 1);
-        const uint4* lw = lds_w + cur * TILE_CHUNKS + wbase;
-        const uint4* lx = lds_x + cur * TILE_CHUNKS + xbase;
+    // One K-tile kt from stage s (its sub-step-0 fragments already in set A;
+    // K-tile kt+1 already requested into the other stage):
+    //   sub-steps 0..2: MFMAs of one fragment set while the next sub-step's
+    //   fragments are read into the other set;
+    //   wait for this wave's loads and LDS reads, workgroup barrier: the other
+    //   stage is complete everywhere, and stage s -- fully read by now -- is free;
+    //   at once request K-tile kt+2 into stage s, so that the memory pipe never
+    //   idles, and read sub-step 0 of K-tile kt+1 under the sub-step-3 MFMAs.
+    // sched_group_barrier pins the interleaving (0x008 MFMA, 0x020 VMEM read,
+    // 0x100 DS read); the asm barrier bounds each scheduling region.
+    const int KT = K / BK;                                  // = 2 * heads: even
+    auto k_tile = [&](int kt, int s) {
+        read_frags(s, 1, fa_b, fb_b);
+        mfmas(fa_a, fb_a);
+        read_frags(s, 2, fa_a, fb_a);
+        mfmas(fa_b, fb_b);
+        read_frags(s, 3, fa_b, fb_b);
+        mfmas(fa_a, fb_a);
 #pragma unroll
-        for (int ks = 0; ks < 4; ++ks) {
-            bf16x8 af[4], bfm[4];
+        for (int r = 0; r < 3; ++r) {
 #pragma unroll
-            for (int b = 0; b < 4; ++b) {
-                af[b] = __builtin_bit_cast(bf16x8, lw[b * 32 * CHUNKS + koff[ks]]);
-                bfm[b] = __builtin_bit_cast(bf16x8, lx[b * 32 * CHUNKS + koff[ks]]);
+            for (int i = 0; i < 8; ++i) {
+                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
             }
-#pragma unroll
-            for (int nb = 0; nb < 4; ++nb)
-#pragma unroll
-                for (int mb = 0; mb < 4; ++mb)
-                    acc[nb][mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[nb], bfm[mb],
-                                                                         acc[nb][mb], 0, 0, 0);
+            __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
         }
-        if (kt + 1 < KT) store_tile(cur ^ 1);
-        __syncthreads();
+        asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+        load_stage(min(kt + 2, KT - 1), s);
+        read_frags(s ^ 1, 0, fa_a, fb_a);
+        mfmas(fa_b, fb_b);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x020, 2, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
+    };
+
+    load_stage(0, 0);
+    load_stage(min(1, KT - 1), 1);
+    asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(2 * LOADS) : "memory");
+    read_frags(0, 0, fa_a, fb_a);
+    for (int kt = 0; kt < KT; kt += 2) {
+        k_tile(kt, 0);
+        k_tile(kt + 1, 1);
     }
+    // the last request re-read the last tile in bounds; drain it before the
+    // workgroup's LDS can be handed to another workgroup
+    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
 
     // ---- epilogue: one head (128 columns) per wave ----------------------------
+    // Accumulator register reg of n-block nb in lane-half hf holds head dim
+    //   e = 64 (nb / 2) + 32 hf + 8 (reg % 4) + 4 (nb % 2) + reg / 4
+    // of the token of MFMA column fr of m-block mb, tile token
+    //   wm * 128 + mfma_row(mb, fr).
+    // Registers q, q+4, q+8, q+12 hold four consecutive dims; n-blocks 2h and
+    // 2h+1 continue each other (16 bytes of bf16); n-block nb+2 holds e + 64.
     const int ncol = n0 + wn * 128;
     if (ncol >= a.N) return;
     const int p = ncol / a.hidden;                 // 0 q, 1 k, 2 v
@@ -184,12 +247,15 @@ void fused_qkv_kernel(FusedArgs a) {
     const int j = h - d * a.local_heads;
     uint16_t* dbase = a.slot + int64_t(d) * a.region_elems + int64_t(p) * a.part_stride +
                       int64_t(j) * a.stride_h;
+    const bool qk = p < 2;
     const float* nw = p == 0 ? a.wq : a.wk;
 
 #pragma unroll
     for (int mb = 0; mb < 4; ++mb) {
-        const int m = m0 + wm * 128 + mb * 32 + fr;
-        if (m >= a.M) continue;
+        // tokens past M (ragged last tile) are computed on token M - 1 and not stored
+        const int m_tile = m0 + wm * 128 + mfma_row(mb, fr);
+        const bool in_range = m_tile < a.M;
+        const int m = in_range ? m_tile : a.M - 1;
         const int bidx = m / a.s_local;
         const int s = m - bidx * a.s_local;
         const int row = a.row0 + s;                 // sequence row == position
@@ -199,7 +265,7 @@ void fused_qkv_kernel(FusedArgs a) {
 #pragma unroll
             for (int r = 0; r < 16; ++r) v[nb][r] = acc[nb][mb][r];
 
-        if (p < 2) {
+        if (qk) {
             // RMSNorm over the head's 128 values: 64 here, 64 in lane ^ 32
             float ss = 0.f;
 #pragma unroll
@@ -208,44 +274,44 @@ void fused_qkv_kernel(FusedArgs a) {
                 for (int r = 0; r < 16; ++r) ss += v[nb][r] * v[nb][r];
             ss += __shfl_xor(ss, 32);
             const float inv = rsqrtf(ss * (1.0f / 128.0f) + a.eps);
-            // value (nb, r) is head dim e = 32 nb + 8 (r / 4) + 4 hf + r % 4
-#pragma unroll
-            for (int nb = 0; nb < 4; ++nb)
-#pragma unroll
-                for (int g = 0; g < 4; ++g) {
-                    const f32x4 wv = *reinterpret_cast<const f32x4*>(nw + 32 * nb + 8 * g + 4 * hf);
-#pragma unroll
-                    for (int q = 0; q < 4; ++q) v[nb][4 * g + q] *= inv * wv[q];
-                }
-            // rotate-half RoPE: dim e < 64 pairs with e + 64 (n-block nb + 2)
             const float* csr = a.cs + int64_t(row) * 128;
+            // n-blocks lo = nb and hi = nb + 2 hold dims e and e + 64
 #pragma unroll
-            for (int nb = 0; nb < 2; ++nb)
+            for (int lo = 0; lo < 2; ++lo) {
+                f32x4 wl[4], wh[4], cv[4], sv[4];
 #pragma unroll
-                for (int g = 0; g < 4; ++g) {
-                    const int e = 32 * nb + 8 * g + 4 * hf;
-                    const f32x4 c = *reinterpret_cast<const f32x4*>(csr + e);
-                    const f32x4 sn = *reinterpret_cast<const f32x4*>(csr + 64 + e);
-#pragma unroll
-                    for (int q = 0; q < 4; ++q) {
-                        const float lo = v[nb][4 * g + q];
-                        const float hi = v[nb + 2][4 * g + q];
-                        v[nb][4 * g + q] = lo * c[q] - hi * sn[q];
-                        v[nb + 2][4 * g + q] = hi * c[q] + lo * sn[q];
-                    }
+                for (int q = 0; q < 4; ++q) {
+                    const int e = 32 * hf + 8 * q + 4 * lo;
+                    wl[q] = *reinterpret_cast<const f32x4*>(nw + e);
+                    wh[q] = *reinterpret_cast<const f32x4*>(nw + 64 + e);
+                    cv[q] = *reinterpret_cast<const f32x4*>(csr + e);
+                    sv[q] = *reinterpret_cast<const f32x4*>(csr + 64 + e);
                 }
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const float zl = v[lo][r] * (inv * wl[r & 3][r >> 2]);
+                    const float zh = v[lo + 2][r] * (inv * wh[r & 3][r >> 2]);
+                    const float c = cv[r & 3][r >> 2];
+                    const float sn = sv[r & 3][r >> 2];
+                    v[lo][r] = zl * c - zh * sn;
+                    v[lo + 2][r] = zh * c + zl * sn;
+                }
+            }
         }
         uint16_t* orow = dbase + int64_t(bidx) * a.stride_b + int64_t(row) * a.stride_s;
 #pragma unroll
-        for (int nb = 0; nb < 4; ++nb)
+        for (int hh = 0; hh < 2; ++hh)
 #pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                const int e = 32 * nb + 8 * g + 4 * hf;
-                uint2 pk;
-                pk.x = uint32_t(bf16_bits(v[nb][4 * g + 0])) | (uint32_t(bf16_bits(v[nb][4 * g + 1])) << 16);
-                pk.y = uint32_t(bf16_bits(v[nb][4 * g + 2])) | (uint32_t(bf16_bits(v[nb][4 * g + 3])) << 16);
-                *reinterpret_cast<uint2*>(orow + e) = pk;
+            for (int q = 0; q < 4; ++q) {
+                const int e = 64 * hh + 32 * hf + 8 * q;
+                uint4 pk;
+                pk.x = uint32_t(bf16_bits(v[2 * hh][q])) | (uint32_t(bf16_bits(v[2 * hh][q + 4])) << 16);
+                pk.y = uint32_t(bf16_bits(v[2 * hh][q + 8])) | (uint32_t(bf16_bits(v[2 * hh][q + 12])) << 16);
+                pk.z = uint32_t(bf16_bits(v[2 * hh + 1][q])) | (uint32_t(bf16_bits(v[2 * hh + 1][q + 4])) << 16);
+                pk.w = uint32_t(bf16_bits(v[2 * hh + 1][q + 8])) | (uint32_t(bf16_bits(v[2 * hh + 1][q + 12])) << 16);
+                if (in_range) *reinterpret_cast<uint4*>(orow + e) = pk;
             }
+        __builtin_amdgcn_sched_barrier(0);
     }
 }
 
