@@ -24,10 +24,13 @@
 //    keeps both the chunk writes and the MFMA fragment reads free of bank
 //    conflicts.  The next K-tile's global loads are in flight while the
 //    current tile's MFMAs run.
-//  * Tiles are enumerated XCD-aware: consecutive workgroups go round-robin to
-//    the 8 XCDs, so each XCD is given a contiguous range of the tile order,
-//    which walks groups of tile rows so that neighbouring tiles share X and W
-//    panels in that XCD's L2.
+//  * Persistent: one workgroup per CU walks its share of the tiles, and the
+//    K-tiles of consecutive output tiles form one continuous load stream, so
+//    the next tile's first K-tiles are in flight while the current tile's
+//    epilogue runs.  In each round the 8 XCDs (workgroup b runs on XCD b % 8)
+//    take consecutive ranges of a tile order that walks groups of tile rows
+//    column by column, so the tiles an XCD runs together share X and W
+//    panels in its L2.
 #include "qkvx_internal.h"
 
 namespace qkvx {
@@ -66,22 +69,15 @@ __device__ __forceinline__ int mfma_row(int nb, int i) {
     return 64 * (nb >> 1) + 8 * (i & 7) + 4 * (nb & 1) + (i >> 3);
 }
 
-__device__ __forceinline__ void tile_coords(int bid, int tiles_m, int tiles_n, int group_m,
+// Tile coordinates of logical tile l: groups of group_m tile rows, walked
+// column by column.
+__device__ __forceinline__ void tile_coords(int l, int tiles_m, int tiles_n, int group_m,
                                             int& tm, int& tn) {
-    const int total = tiles_m * tiles_n;
-    // XCD-aware remap: workgroup bid runs on XCD bid % 8; give each XCD a
-    // contiguous range of the logical order.
-    const int xcd = bid % NXCD;
-    const int idx = bid / NXCD;
-    const int per = total / NXCD;
-    const int rem = total % NXCD;
-    const int logical = xcd < rem ? xcd * (per + 1) + idx : rem * (per + 1) + (xcd - rem) * per + idx;
-    // grouped order: walk group_m tile rows column by column
     const int in_group = group_m * tiles_n;
-    const int g = logical / in_group;
+    const int g = l / in_group;
     const int first_m = g * group_m;
     const int gsize = min(tiles_m - first_m, group_m);
-    const int r = logical - g * in_group;
+    const int r = l - g * in_group;
     tm = first_m + r % gsize;
     tn = r / gsize;
 }
@@ -103,11 +99,35 @@ void fused_qkv_kernel(FusedArgs a) {
     const int wn = wave & 1;      // which head of the tile
     const int wm = wave >> 1;     // which 128 tokens of the tile
 
-    int tm, tn;
-    tile_coords(blockIdx.x, a.tiles_m, a.tiles_n, a.group_m, tm, tn);
-    const int m0 = tm * BM;
-    const int n0 = tn * BN;
+    // ---- tile schedule ---------------------------------------------------------
+    // XCD x (workgroups b with b % 8 == x) owns a contiguous eighth of the
+    // logical tile order; its G/8 workgroups walk that range G/8 tiles at a
+    // time, so the 8 XCDs sweep the W panels at the same pace (sharing them
+    // through the last-level cache) while each XCD's concurrent tiles share
+    // panels in its L2.
+    const int G = gridDim.x;
+    const int bid = blockIdx.x;
+    const int total = a.tiles_m * a.tiles_n;
+    int first, stride, end;
+    if (G % NXCD == 0) {
+        const int x = bid % NXCD;
+        const int per = total / NXCD, rem = total % NXCD;
+        first = x * per + min(x, rem) + bid / NXCD;
+        end = (x + 1) * per + min(x + 1, rem);
+        stride = G / NXCD;
+    } else {
+        first = bid;
+        end = total;
+        stride = G;
+    }
+    if (first >= end) return;
     const int K = a.K;
+    auto tile_origin = [&](int l, int& m0, int& n0) {
+        int tm, tn;
+        tile_coords(l, a.tiles_m, a.tiles_n, a.group_m, tm, tn);
+        m0 = tm * BM;
+        n0 = tn * BN;
+    };
 
     // ---- global -> LDS: direct loads (buffer_load ... lds) ----------------------
     // Instruction i of wave w fills block b = 4 i + w of a stage: lane L brings
@@ -120,8 +140,11 @@ void fused_qkv_kernel(FusedArgs a) {
     const uint32_t rowbytes = uint32_t(K) * 2u;
     const int wv = wave;
     const uint32_t lrow = uint32_t(8 * wv + (lane >> 3));
-    const uint32_t gw0 = (uint32_t(n0) + lrow) * rowbytes + uint32_t(lane & 7) * 16u;
-    const uint32_t gx0 = (uint32_t(m0) + lrow) * rowbytes + uint32_t(lane & 7) * 16u;
+    // this lane's byte offset of K-tile 0 of a tile's W panel (origin n0) or X
+    // panel (origin m0)
+    auto panel_offset = [&](int origin) {
+        return (uint32_t(origin) + lrow) * rowbytes + uint32_t(lane & 7) * 16u;
+    };
 
     // ---- fragment reads: lane i%32 owns MFMA row i%32 of each 32-row block ----
     const int fr = lane & 31;
@@ -134,15 +157,10 @@ void fused_qkv_kernel(FusedArgs a) {
     }
 
     f32x16 acc[4][4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-    // Request K-tile kt into stage s: 2 x LOADS block loads per wave.
-    auto load_stage = [&](int kt, int s) {
+    // Request K-tile kt of the panels at (gw0, gx0) into stage s: 2 x LOADS
+    // block loads per wave.
+    auto load_stage = [&](uint32_t gw0, uint32_t gx0, int kt, int s) {
         const uint32_t kb = uint32_t(kt) * BK * 2u;
         typedef __attribute__((address_space(3))) uint4 lds_uint4;
         lds_uint4* dw = (lds_uint4*)((s ? lw1 : lw0) + wv * BLOCK_CHUNKS);
@@ -180,57 +198,66 @@ void fused_qkv_kernel(FusedArgs a) {
                                                                      0, 0, 0);
     };
 
-    // One K-tile kt from stage s (its sub-step-0 fragments already in set A;
-    // K-tile kt+1 already requested into the other stage):
-    //   sub-steps 0..2: MFMAs of one fragment set while the next sub-step's
-    //   fragments are read into the other set;
-    //   wait for this wave's loads and LDS reads, workgroup barrier: the other
-    //   stage is complete everywhere, and stage s -- fully read by now -- is free;
-    //   at once request K-tile kt+2 into stage s, so that the memory pipe never
-    //   idles, and read sub-step 0 of K-tile kt+1 under the sub-step-3 MFMAs.
+    // ---- main loop ------------------------------------------------------------
+    // The K-tiles of this workgroup's output tiles form one stream.  The code
+    // between two workgroup barriers (one scheduling region) handles K-tile kt
+    // in stage s = kt % 2:
+    //   the sub-step-3 MFMAs of K-tile kt-1 (its fragments are in set B);
+    //   the loads of K-tile kt+1 into the other stage (free since the barrier),
+    //   one instruction per two MFMAs over the first half of the region, so
+    //   that the address unit never fills up and stalls the wave's in-order
+    //   MFMA issue, while the last load still has half a region to arrive;
+    //   the fragment reads of K-tile kt's four sub-steps and the MFMAs of its
+    //   sub-steps 0..2, each sub-step's reads overlapping the previous MFMAs;
+    // then a wait for this wave's loads and LDS reads, and the barrier.
     // sched_group_barrier pins the interleaving (0x008 MFMA, 0x020 VMEM read,
-    // 0x100 DS read); the asm barrier bounds each scheduling region.
+    // 0x100 DS read).
     const int KT = K / BK;                                  // = 2 * heads: even
-    auto k_tile = [&](int kt, int s) {
+    // Panels of the current tile and of this workgroup's next tile; past its
+    // last tile the "next" requests re-read the current tile (in bounds, unused).
+    int m0, n0, m0_next, n0_next;
+    tile_origin(first, m0, n0);
+    int next = first + stride;
+    tile_origin(next < end ? next : first, m0_next, n0_next);
+    uint32_t gw_cur = panel_offset(n0), gx_cur = panel_offset(m0);
+    uint32_t gw_nxt = panel_offset(n0_next), gx_nxt = panel_offset(m0_next);
+    // load K-tile index kidx of the stream (kidx >= KT: the next output tile)
+    auto load_k = [&](int kidx, int stage) {
+        const bool nx = kidx >= KT;
+        load_stage(nx ? gw_nxt : gw_cur, nx ? gx_nxt : gx_cur, nx ? kidx - KT : kidx, stage);
+    };
+
+    // Region of K-tile kt (stage s); `steady` adds the previous K-tile's
+    // sub-step-3 MFMAs and the loads of K-tile kt + 1.
+    auto region = [&](int kt, int s, bool steady) {
+        if (steady) {
+            mfmas(fa_b, fb_b);
+            load_k(kt + 1, s ^ 1);
+        }
+        read_frags(s, 0, fa_a, fb_a);
         read_frags(s, 1, fa_b, fb_b);
         mfmas(fa_a, fb_a);
         read_frags(s, 2, fa_a, fb_a);
         mfmas(fa_b, fb_b);
         read_frags(s, 3, fa_b, fb_b);
         mfmas(fa_a, fb_a);
+        if (steady) {
 #pragma unroll
-        for (int r = 0; r < 3; ++r) {
-#pragma unroll
-            for (int i = 0; i < 8; ++i) {
+            for (int i = 0; i < 16; ++i) {
+                __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
                 __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
             }
-            __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
+        } else {
+            __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+        }
+#pragma unroll
+        for (int i = 0; i < (steady ? 16 : 24); ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
         }
         asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
-        load_stage(min(kt + 2, KT - 1), s);
-        read_frags(s ^ 1, 0, fa_a, fb_a);
-        mfmas(fa_b, fb_b);
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            __builtin_amdgcn_sched_group_barrier(0x020, 2, 0);
-            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        }
-        __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
     };
-
-    load_stage(0, 0);
-    load_stage(min(1, KT - 1), 1);
-    asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(2 * LOADS) : "memory");
-    read_frags(0, 0, fa_a, fb_a);
-    for (int kt = 0; kt < KT; kt += 2) {
-        k_tile(kt, 0);
-        k_tile(kt + 1, 1);
-    }
-    // the last request re-read the last tile in bounds; drain it before the
-    // workgroup's LDS can be handed to another workgroup
-    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
 
     // ---- epilogue: one head (128 columns) per wave ----------------------------
     // Accumulator register reg of n-block nb in lane-half hf holds head dim
@@ -239,6 +266,7 @@ void fused_qkv_kernel(FusedArgs a) {
     //   wm * 128 + mfma_row(mb, fr).
     // Registers q, q+4, q+8, q+12 hold four consecutive dims; n-blocks 2h and
     // 2h+1 continue each other (16 bytes of bf16); n-block nb+2 holds e + 64.
+  auto epilogue = [&](int m0, int n0) {
     const int ncol = n0 + wn * 128;
     if (ncol >= a.N) return;
     const int p = ncol / a.hidden;                 // 0 q, 1 k, 2 v
@@ -259,11 +287,15 @@ void fused_qkv_kernel(FusedArgs a) {
         const int bidx = m / a.s_local;
         const int s = m - bidx * a.s_local;
         const int row = a.row0 + s;                 // sequence row == position
+        // Accumulators are read out of AGPRs one m-block at a time; written as
+        // explicit reads so that the compiler does not copy all 256 of them into
+        // VGPRs at the loop exit (which would spill).
         float v[4][16];
 #pragma unroll
         for (int nb = 0; nb < 4; ++nb)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) v[nb][r] = acc[nb][mb][r];
+            for (int r = 0; r < 16; ++r)
+                asm volatile("v_accvgpr_read_b32 %0, %1" : "=v"(v[nb][r]) : "a"(acc[nb][mb][r]));
 
         if (qk) {
             // RMSNorm over the head's 128 values: 64 here, 64 in lane ^ 32
@@ -313,11 +345,69 @@ void fused_qkv_kernel(FusedArgs a) {
             }
         __builtin_amdgcn_sched_barrier(0);
     }
+  };
+
+
+    // prologue: K-tiles 0 and 1 of the first tile
+    load_stage(gw_cur, gx_cur, 0, 0);
+    load_stage(gw_cur, gx_cur, 1, 1);
+    asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(2 * LOADS) : "memory");
+    for (;;) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+        // K-tile 1 was requested before this tile began (it overlapped the
+        // previous epilogue); K-tile 2 on is requested one region ahead
+        region(0, 0, false);
+        region(1, 1, true);
+        for (int kt = 2; kt < KT; kt += 2) {
+            region(kt, 0, true);
+            region(kt + 1, 1, true);
+        }
+        // the next tile's K-tile 0 is in stage 0; request its K-tile 1 into the
+        // (free) stage 1 so that it loads during the epilogue
+        load_k(KT + 1, 1);
+        mfmas(fa_b, fb_b);                          // sub-step 3 of the last K-tile
+        // the nops give the last MFMAs' results the wait states an accumulator
+        // read needs
+        asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
+        epilogue(m0, n0);
+        if (next >= end) break;
+        m0 = m0_next;
+        n0 = n0_next;
+        gw_cur = gw_nxt;
+        gx_cur = gx_nxt;
+        next += stride;
+        tile_origin(next < end ? next : next - stride, m0_next, n0_next);
+        gw_nxt = panel_offset(n0_next);
+        gx_nxt = panel_offset(m0_next);
+    }
+    // drain the requests of the (non-existent) tile after the last one before
+    // the workgroup's LDS can be handed to another workgroup
+    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
 }
 
 }  // namespace
 
 FusedPlan fused_plan() { return FusedPlan{BM, BN, BK, NT, GROUP_M}; }
+
+// Compute units of the current device (cached per device).
+static int device_cus() {
+    static int cache[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    if (cache[dev] == 0) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+            n <= 0)
+            n = 256;
+        cache[dev] = n;
+    }
+    return cache[dev];
+}
 
 hipError_t launch_fused(const FusedArgs& a_in, hipStream_t stream) {
     FusedArgs a = a_in;
@@ -325,7 +415,8 @@ hipError_t launch_fused(const FusedArgs& a_in, hipStream_t stream) {
     a.tiles_n = (a.N + BN - 1) / BN;
     a.group_m = GROUP_M;
     const int tiles = a.tiles_m * a.tiles_n;
-    hipLaunchKernelGGL(fused_qkv_kernel, dim3(tiles), dim3(NT), 0, stream, a);
+    const int grid = tiles < device_cus() ? tiles : device_cus();
+    hipLaunchKernelGGL(fused_qkv_kernel, dim3(grid), dim3(NT), 0, stream, a);
     return hipGetLastError();
 }
 
