@@ -11,69 +11,57 @@
 // The peer index (d or u) is blockIdx.y, so the peer's base pointer is a
 // wave-uniform kernel argument and no per-lane table lookup is needed; the rest
 // of the flat 16-byte-chunk index is split with precomputed 32-bit dividers.
+// Each thread moves one 16-byte vector with nontemporal accesses.
 #include "qkvx_internal.h"
 
 namespace qkvx {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kVec = 4;   // 16-byte chunks per thread: four loads in flight before the stores
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+// One 16-byte vector per thread, nontemporal on both sides: the data is used
+// once, so it should neither displace the caches' working set nor wait for it;
+// on MI355X this form gives the highest copy rate (many short-lived waves,
+// every request streaming).
+__device__ __forceinline__ u32x4 load_nt(const uint16_t* p) {
+    return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+}
+__device__ __forceinline__ void store_nt(uint16_t* p, u32x4 v) {
+    __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(p));
+}
 
 __global__ __launch_bounds__(kThreads) void pack_kernel(PackArgs a) {
     const uint32_t d = blockIdx.y;
-    uint16_t* __restrict__ dst = a.dst[d];
-    const uint32_t first = blockIdx.x * (kThreads * kVec) + threadIdx.x;
-    uint4 val[kVec];
-    uint16_t* ptr[kVec];
-#pragma unroll
-    for (int i = 0; i < kVec; ++i) {
-        const uint32_t c = first + i * kThreads;
-        ptr[i] = nullptr;
-        if (c < a.total) {
-            const uint32_t e16 = c & 15u;
-            uint32_t u = c >> 4;
-            const uint32_t p = u % 3u;            // q, k, v interleaved per head
-            u = u / 3u;
-            uint32_t tok, j, b, s;
-            a.div_hc.divmod(u, tok, j);
-            a.div_s.divmod(tok, b, s);
-            const uint16_t* src = p == 0 ? a.src[0] : (p == 1 ? a.src[1] : a.src[2]);
-            const int64_t sb = p == 0 ? a.sb[0] : (p == 1 ? a.sb[1] : a.sb[2]);
-            const int64_t ss = p == 0 ? a.ss[0] : (p == 1 ? a.ss[1] : a.ss[2]);
-            const int64_t sh = p == 0 ? a.sh[0] : (p == 1 ? a.sh[1] : a.sh[2]);
-            src += b * sb + s * ss + int64_t(d * a.local_heads + j) * sh + e16 * 8;
-            val[i] = *reinterpret_cast<const uint4*>(src);
-            ptr[i] = dst + b * a.db + s * a.ds + j * a.dh + p * 128 + e16 * 8;
-        }
-    }
-#pragma unroll
-    for (int i = 0; i < kVec; ++i)
-        if (ptr[i]) *reinterpret_cast<uint4*>(ptr[i]) = val[i];
+    const uint32_t c = blockIdx.x * kThreads + threadIdx.x;
+    if (c >= a.total) return;
+    const uint32_t e16 = c & 15u;
+    uint32_t u = c >> 4;
+    const uint32_t p = u % 3u;                     // q, k, v interleaved per head
+    u = u / 3u;
+    uint32_t tok, j, b, s;
+    a.div_hc.divmod(u, tok, j);
+    a.div_s.divmod(tok, b, s);
+    const uint16_t* src = p == 0 ? a.src[0] : (p == 1 ? a.src[1] : a.src[2]);
+    const int64_t sb = p == 0 ? a.sb[0] : (p == 1 ? a.sb[1] : a.sb[2]);
+    const int64_t ss = p == 0 ? a.ss[0] : (p == 1 ? a.ss[1] : a.ss[2]);
+    const int64_t sh = p == 0 ? a.sh[0] : (p == 1 ? a.sh[1] : a.sh[2]);
+    src += b * sb + s * ss + int64_t(d * a.local_heads + j) * sh + e16 * 8;
+    uint16_t* dst = a.dst[d] + b * a.db + s * a.ds + j * a.dh + p * 128 + e16 * 8;
+    store_nt(dst, load_nt(src));
 }
 
 __global__ __launch_bounds__(kThreads) void merge_kernel(MergeArgs a) {
     const uint32_t u = blockIdx.y;
-    const uint16_t* __restrict__ src = a.src[u];
-    uint16_t* __restrict__ out = a.out + int64_t(u) * a.local_heads * 128;
-    const uint32_t first = blockIdx.x * (kThreads * kVec) + threadIdx.x;
-    uint4 val[kVec];
-    uint16_t* ptr[kVec];
-#pragma unroll
-    for (int i = 0; i < kVec; ++i) {
-        const uint32_t c = first + i * kThreads;
-        ptr[i] = nullptr;
-        if (c < a.total) {
-            const uint32_t e16 = c & 15u;
-            uint32_t tok, j, b, s;
-            a.div_hc.divmod(c >> 4, tok, j);
-            a.div_s.divmod(tok, b, s);
-            val[i] = *reinterpret_cast<const uint4*>(src + b * a.sb + s * a.ss + j * a.sh + e16 * 8);
-            ptr[i] = out + b * a.ob + s * a.os + j * 128 + e16 * 8;
-        }
-    }
-#pragma unroll
-    for (int i = 0; i < kVec; ++i)
-        if (ptr[i]) *reinterpret_cast<uint4*>(ptr[i]) = val[i];
+    const uint32_t c = blockIdx.x * kThreads + threadIdx.x;
+    if (c >= a.total) return;
+    const uint32_t e16 = c & 15u;
+    uint32_t tok, j, b, s;
+    a.div_hc.divmod(c >> 4, tok, j);
+    a.div_s.divmod(tok, b, s);
+    const uint16_t* src = a.src[u] + b * a.sb + s * a.ss + j * a.sh + e16 * 8;
+    uint16_t* out = a.out + int64_t(u) * a.local_heads * 128 + b * a.ob + s * a.os + j * 128 + e16 * 8;
+    store_nt(out, load_nt(src));
 }
 
 __global__ __launch_bounds__(kThreads) void fill16_kernel(uint16_t* p, int64_t n, uint32_t pattern) {
@@ -91,7 +79,7 @@ __global__ __launch_bounds__(kThreads) void fill16_kernel(uint16_t* p, int64_t n
 
 hipError_t launch_pack(const PackArgs& a, int world, hipStream_t stream) {
     if (a.total == 0) return hipSuccess;
-    const uint32_t per_block = kThreads * kVec;
+    const uint32_t per_block = kThreads;
     dim3 grid((a.total + per_block - 1) / per_block, world);
     hipLaunchKernelGGL(pack_kernel, grid, dim3(kThreads), 0, stream, a);
     return hipGetLastError();
@@ -99,7 +87,7 @@ hipError_t launch_pack(const PackArgs& a, int world, hipStream_t stream) {
 
 hipError_t launch_merge(const MergeArgs& a, int world, hipStream_t stream) {
     if (a.total == 0) return hipSuccess;
-    const uint32_t per_block = kThreads * kVec;
+    const uint32_t per_block = kThreads;
     dim3 grid((a.total + per_block - 1) / per_block, world);
     hipLaunchKernelGGL(merge_kernel, grid, dim3(kThreads), 0, stream, a);
     return hipGetLastError();
