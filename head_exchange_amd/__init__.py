@@ -17,6 +17,7 @@ LIB_PATH = os.path.join(HERE, "libqkvx.so")
 HEAD_DIM = 128
 MAX_WORLD = 64
 LAYOUTS = {"bshd": 0, "fused": 1}
+ROPES = {"rotate_half": 0, "interleaved": 1}
 
 QKVX_OK = 0
 STATUS = {0: "OK", -1: "INVALID", -2: "DIVISIBILITY", -3: "CAPACITY", -4: "ALIGNMENT",
@@ -81,7 +82,7 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.qkvx_slot_bytes.restype = sz
     lib.qkvx_slot_bytes.argtypes = [i32, i32, i64, i32]
     lib.qkvx_create.restype = i32
-    lib.qkvx_create.argtypes = [i32, i32, i32, i32, i32, i64, i32, vp, sz, ctypes.POINTER(vp)]
+    lib.qkvx_create.argtypes = [i32, i32, i32, i32, i32, i32, i64, i32, vp, sz, ctypes.POINTER(vp)]
     lib.qkvx_forward.restype = i32
     lib.qkvx_forward.argtypes = [vp, vp, i32, i32, vp, vp, vp, vp, i64, i32, vp,
                                  ctypes.POINTER(Outputs)]
@@ -183,20 +184,24 @@ class Session:
 
     def __init__(self, hidden: int, num_heads: int, head_dim: int = HEAD_DIM, world: int = 1,
                  layout: str = "bshd", max_tokens: int = 1, num_slots: int = 2,
-                 device=None):
+                 device=None, rope: str = "rotate_half"):
         import torch
         lib = load()
         if layout not in LAYOUTS:
             raise QkvxValueError(-7, f"layout {layout!r} is neither 'bshd' nor 'fused'")
+        if rope not in ROPES:
+            raise QkvxValueError(-1, f"rope {rope!r} is neither 'rotate_half' nor 'interleaved'")
         self.hidden, self.num_heads, self.world = hidden, num_heads, world
         self.layout, self.max_tokens, self.num_slots = layout, max_tokens, num_slots
+        self.rope = rope
         nbytes = lib.qkvx_slot_bytes(hidden, world, max_tokens, num_slots)
         device = torch.device("cuda") if device is None else torch.device(device)
         # 256-byte alignment: torch's allocator returns 512-byte aligned blocks
         self.slots = torch.empty(max(nbytes // 2, 1), dtype=torch.uint16, device=device)
         h = ctypes.c_void_p()
-        _check(lib.qkvx_create(hidden, num_heads, head_dim, world, LAYOUTS[layout], max_tokens,
-                               num_slots, self.slots.data_ptr(), nbytes, ctypes.byref(h)))
+        _check(lib.qkvx_create(hidden, num_heads, head_dim, world, LAYOUTS[layout], ROPES[rope],
+                               max_tokens, num_slots, self.slots.data_ptr(), nbytes,
+                               ctypes.byref(h)))
         self._h = h
         self._last = None
 
@@ -268,8 +273,9 @@ class Session:
 
 def qkvx_create(hidden: int, num_heads: int, head_dim: int = HEAD_DIM, world: int = 1,
                 layout: str = "bshd", max_tokens: int = 1, num_slots: int = 2,
-                device=None) -> Session:
-    return Session(hidden, num_heads, head_dim, world, layout, max_tokens, num_slots, device)
+                device=None, rope: str = "rotate_half") -> Session:
+    return Session(hidden, num_heads, head_dim, world, layout, max_tokens, num_slots, device,
+                   rope)
 
 
 def qkvx_forward(session: Session, x, w_qkv, q_norm_w, k_norm_w, cos_sin, rank: int,

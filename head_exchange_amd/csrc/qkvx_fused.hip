@@ -5,7 +5,8 @@
 // comm.html, "Fused QKV Projection + Norm + RoPE + Head Exchange"; the QKV
 // exchange pull request body, "Assumptions": projection -> QK-norm -> RoPE,
 // fp32 norm with eps 1e-6 and one [head_dim] weight for Q and one for K, bf16
-// operands and outputs), with RoPE pairing lanes i and i+64.
+// operands and outputs), with RoPE pairing lanes i and i+64 (rotate-half) or,
+// as in the pages' operator, lanes 2i and 2i+1 (interleaved).
 //
 // Design (gfx950):
 //  * The GEMM is computed transposed, C^T[n, m] = W[n, :] . X[m, :], with
@@ -52,6 +53,7 @@ constexpr int LOADS = 32 / 4;                  // block loads per wave per opera
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 
 // LDS chunk index of chunk c of tile row r of one operand stage: block r / 8
 // holds rows 8 (r / 8) .. + 7 as 128 contiguous bytes each, and every 1 KB block
@@ -307,7 +309,34 @@ void fused_qkv_kernel(FusedArgs a) {
             ss += __shfl_xor(ss, 32);
             const float inv = rsqrtf(ss * (1.0f / 128.0f) + a.eps);
             const float* csr = a.cs + int64_t(row) * 128;
-            // n-blocks lo = nb and hi = nb + 2 hold dims e and e + 64
+            if (a.rope_interleaved) {
+                // pairs (2i, 2i+1): registers q + 4 g hold dims E + g, E = e(nb, q), so
+                // (E, E+1) and (E+2, E+3) sit in registers (q, q+4) and (q+8, q+12)
+                // and rotate by the angles of columns E/2 and E/2 + 1
+#pragma unroll
+                for (int nb = 0; nb < 4; ++nb) {
+                    f32x4 wt[4];
+                    f32x2 cv[4], sv[4];
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        const int e = 64 * (nb >> 1) + 32 * hf + 8 * q + 4 * (nb & 1);
+                        wt[q] = *reinterpret_cast<const f32x4*>(nw + e);
+                        cv[q] = *reinterpret_cast<const f32x2*>(csr + e / 2);
+                        sv[q] = *reinterpret_cast<const f32x2*>(csr + 64 + e / 2);
+                    }
+#pragma unroll
+                    for (int q = 0; q < 4; ++q)
+#pragma unroll
+                        for (int gp = 0; gp < 2; ++gp) {
+                            const int r0 = q + 8 * gp, r1 = r0 + 4;
+                            const float z0 = v[nb][r0] * (inv * wt[q][2 * gp]);
+                            const float z1 = v[nb][r1] * (inv * wt[q][2 * gp + 1]);
+                            v[nb][r0] = z0 * cv[q][gp] - z1 * sv[q][gp];
+                            v[nb][r1] = z1 * cv[q][gp] + z0 * sv[q][gp];
+                        }
+                }
+            } else
+            // rotate-half: n-blocks lo = nb and hi = nb + 2 hold dims e and e + 64
 #pragma unroll
             for (int lo = 0; lo < 2; ++lo) {
                 f32x4 wl[4], wh[4], cv[4], sv[4];

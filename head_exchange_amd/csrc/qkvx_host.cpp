@@ -137,7 +137,7 @@ Range peers_touched(const qkvx_peers* p, int u, int64_t batch, int64_t s, int he
 // ===========================================================================
 
 struct qkvx_session {
-    int hidden, heads, world, layout, num_slots;
+    int hidden, heads, world, layout, rope, num_slots;
     int64_t max_tokens;
     int64_t region_elems;       // max_tokens * 3 * hidden
     uint16_t* slots;            // num_slots * world regions
@@ -157,7 +157,7 @@ size_t qkvx_slot_bytes(int hidden, int world, int64_t max_tokens, int num_slots)
     return size_t(num_slots) * size_t(world) * size_t(max_tokens) * 3u * size_t(hidden) * 2u;
 }
 
-int qkvx_create(int hidden, int num_heads, int head_dim, int world, int layout,
+int qkvx_create(int hidden, int num_heads, int head_dim, int world, int layout, int rope,
                 int64_t max_tokens, int num_slots, void* slot_memory, size_t slot_bytes,
                 qkvx_session** out) {
     if (!out) return fail(QKVX_ERR_INVALID, "out is NULL");
@@ -175,6 +175,9 @@ int qkvx_create(int hidden, int num_heads, int head_dim, int world, int layout,
                     num_heads, world);
     if (layout != QKVX_LAYOUT_BSHD && layout != QKVX_LAYOUT_FUSED)
         return fail(QKVX_ERR_LAYOUT, "layout %d is neither bshd (0) nor fused (1)", layout);
+    if (rope != QKVX_ROPE_ROTATE_HALF && rope != QKVX_ROPE_INTERLEAVED)
+        return fail(QKVX_ERR_INVALID, "rope %d is neither rotate-half (0) nor interleaved (1)",
+                    rope);
     if (max_tokens < 1) return fail(QKVX_ERR_INVALID, "max_tokens must be >= 1");
     if (num_slots < 1) return fail(QKVX_ERR_INVALID, "num_slots must be >= 1");
     // operands: x [M, hidden], W [3 hidden, hidden]; byte offsets of padded
@@ -210,6 +213,7 @@ int qkvx_create(int hidden, int num_heads, int head_dim, int world, int layout,
     s->heads = num_heads;
     s->world = world;
     s->layout = layout;
+    s->rope = rope;
     s->num_slots = num_slots;
     s->max_tokens = max_tokens;
     s->region_elems = region;
@@ -319,6 +323,7 @@ int qkvx_forward(qkvx_session* s, const void* x, int batch, int s_local, const v
     a.local_heads = s->heads / s->world;
     a.s_local = s_local;
     a.row0 = rank * s_local;
+    a.rope_interleaved = s->rope == QKVX_ROPE_INTERLEAVED;
     a.eps = 1e-6f;
     hipError_t e = launch_fused(a, static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return hip_fail(e, "fused projection launch");
@@ -353,13 +358,14 @@ int qkvx_describe(const qkvx_session* s, char* buf, size_t len) {
         "{\"hidden\": %d, \"num_heads\": %d, \"head_dim\": %d, \"world\": %d, "
         "\"local_heads\": %d, \"layout\": \"%s\", \"max_tokens\": %lld, \"num_slots\": %d, "
         "\"region_elems\": %lld, \"slot_bytes\": %zu, \"owns_slots\": %s, \"calls\": %lld, "
-        "\"next_slot\": %d, \"rope\": \"rotate_half\", \"eps\": 1e-6, "
+        "\"next_slot\": %d, \"rope\": \"%s\", \"eps\": 1e-6, "
         "\"tile\": {\"block_m\": %d, \"block_n\": %d, \"block_k\": %d, \"threads\": %d, "
         "\"group_m\": %d, \"mfma\": \"v_mfma_f32_32x32x16_bf16\", \"xcd_remap\": 8}}",
         s->hidden, s->heads, QKVX_HEAD_DIM, s->world, s->heads / s->world,
         s->layout == QKVX_LAYOUT_BSHD ? "bshd" : "fused", (long long)s->max_tokens,
         s->num_slots, (long long)s->region_elems, s->slot_bytes, s->owns_slots ? "true" : "false",
-        (long long)s->calls, int(s->calls % s->num_slots), p.block_m, p.block_n, p.block_k,
+        (long long)s->calls, int(s->calls % s->num_slots),
+        s->rope == QKVX_ROPE_INTERLEAVED ? "interleaved" : "rotate_half", p.block_m, p.block_n, p.block_k,
         p.threads, p.group_m);
     if (buf && len) {
         size_t c = size_t(n) < len ? size_t(n) : len - 1;

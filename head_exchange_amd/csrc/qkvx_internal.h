@@ -62,6 +62,7 @@ struct FusedArgs {
     int32_t row0;             // rank * s_local: first sequence row and position
     int32_t tiles_m, tiles_n;
     int32_t group_m;          // tile-row group of the tile order
+    int32_t rope_interleaved; // 0: pairs (i, i + 64); 1: pairs (2i, 2i + 1)
     float eps;
 };
 

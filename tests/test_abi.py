@@ -55,11 +55,11 @@ def test_status_codes_match_header():
 
 
 def create(lib, hidden=512, heads=4, world=2, layout=0, max_tokens=64, slots=2,
-           mem=FAKE, nbytes=None):
+           mem=FAKE, nbytes=None, rope=0):
     h = ctypes.c_void_p()
     if nbytes is None:
         nbytes = lib.qkvx_slot_bytes(hidden, world, max_tokens, slots)
-    st = lib.qkvx_create(hidden, heads, 128, world, layout, max_tokens, slots,
+    st = lib.qkvx_create(hidden, heads, 128, world, layout, rope, max_tokens, slots,
                          ctypes.c_void_p(mem), nbytes, ctypes.byref(h))
     return st, h
 
@@ -75,6 +75,7 @@ def test_slot_bytes(lib):
     (dict(world=0), -1),
     (dict(world=65), -1),
     (dict(layout=2), -7),
+    (dict(rope=2), -1),
     (dict(max_tokens=0), -1),
     (dict(slots=0), -1),
     (dict(nbytes=100), -3),                    # caller memory too small
@@ -96,6 +97,13 @@ def test_create_and_describe_without_device(lib):
     lib.qkvx_describe(h, buf, n + 1)
     d = json.loads(buf.value.decode())
     assert d["local_heads"] == 2 and d["owns_slots"] is False and d["next_slot"] == 0
+    assert d["rope"] == "rotate_half"
+    assert lib.qkvx_destroy(h) == 0
+    st, h = create(lib, rope=1)
+    n = lib.qkvx_describe(h, None, 0)
+    buf = ctypes.create_string_buffer(n + 1)
+    lib.qkvx_describe(h, buf, n + 1)
+    assert json.loads(buf.value.decode())["rope"] == "interleaved"
     o = hx.Outputs()
     assert lib.qkvx_last_outputs(h, ctypes.byref(o)) == -1
     assert lib.qkvx_destroy(h) == 0

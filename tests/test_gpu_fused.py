@@ -33,9 +33,9 @@ class Inputs:
         self.dwq, self.dwk, self.dcs = f32_dev(self.wq), f32_dev(self.wk), f32_dev(self.cs)
 
 
-def make_session(hx, wl: W.Workload, max_tokens=None, num_slots=None):
+def make_session(hx, wl: W.Workload, max_tokens=None, num_slots=None, rope="rotate_half"):
     return hx.qkvx_create(wl.hidden, wl.heads, 128, wl.world, wl.layout,
-                          max_tokens or wl.tokens, num_slots or wl.num_slots)
+                          max_tokens or wl.tokens, num_slots or wl.num_slots, rope=rope)
 
 
 def run(sess, inp: Inputs, rank=None):
@@ -43,13 +43,13 @@ def run(sess, inp: Inputs, rank=None):
                         inp.wl.rank if rank is None else rank)
 
 
-def oracle_rows(inp: Inputs, tokens: np.ndarray, rank: int) -> np.ndarray:
+def oracle_rows(inp: Inputs, tokens: np.ndarray, rank: int, rope="rotate_half") -> np.ndarray:
     """Oracle float64 [T, 3, H, 128] for flat token indices of the shard."""
     wl = inp.wl
     x2 = inp.x.reshape(wl.tokens, wl.hidden)
     s = tokens % wl.s_local
     pos = rank * wl.s_local + s
-    return O.front_end_rows(x2[tokens], inp.w, inp.wq, inp.wk, inp.cs[pos], wl.heads)
+    return O.front_end_rows(x2[tokens], inp.w, inp.wq, inp.wk, inp.cs[pos], wl.heads, rope)
 
 
 def sample_tokens(wl: W.Workload, n: int = 48, seed: int = 0) -> np.ndarray:
@@ -63,19 +63,20 @@ def sample_tokens(wl: W.Workload, n: int = 48, seed: int = 0) -> np.ndarray:
     return np.array(sorted(c for c in cand if 0 <= c < M))
 
 
-def check_sampled(views, inp: Inputs, rank: int, tokens: np.ndarray, label: str):
+def check_sampled(views, inp: Inputs, rank: int, tokens: np.ndarray, label: str,
+                  rope="rotate_half"):
     wl = inp.wl
     got = slot_rows(views, wl.layout, tokens // wl.s_local, rank * wl.s_local + tokens % wl.s_local)
-    ref = oracle_rows(inp, tokens, rank)
+    ref = oracle_rows(inp, tokens, rank, rope)
     for p, name in enumerate("qkv"):
         check_fp(got[:, p], ref[:, p], f"{label}:{name}")
 
 
-def check_full(views, inp: Inputs, rank: int, label: str, poison=True):
+def check_full(views, inp: Inputs, rank: int, label: str, poison=True, rope="rotate_half"):
     """Whole slots: this rank's rows match the oracle, every other row still
     holds the poison pattern."""
     wl = inp.wl
-    vals = O.front_end_values(inp.x, inp.w, inp.wq, inp.wk, inp.cs, wl.heads, rank)
+    vals = O.front_end_values(inp.x, inp.w, inp.wq, inp.wk, inp.cs, wl.heads, rank, rope)
     got = slot_full(views, wl.layout)
     r0, r1 = rank * wl.s_local, (rank + 1) * wl.s_local
     hl = wl.local_heads
@@ -116,6 +117,27 @@ def test_small_full_slots(gpu_lib, wl):
     views = run(sess, inp)
     torch.cuda.synchronize()
     check_full(views, inp, wl.rank, wl.name)
+
+
+@pytest.mark.parametrize("wl", SMALL[:3], ids=lambda w: w.name)
+def test_small_full_slots_interleaved_rope(gpu_lib, wl):
+    """The pages' pairing (2i, 2i+1) selected at session creation."""
+    inp = Inputs(wl)
+    sess = make_session(gpu_lib, wl, rope="interleaved")
+    sess.poison_receive_slots()
+    views = run(sess, inp)
+    torch.cuda.synchronize()
+    check_full(views, inp, wl.rank, wl.name + ":interleaved", rope="interleaved")
+
+
+def test_full_size_sampled_interleaved_rope(gpu_lib):
+    wl = W.WORKLOADS["h56_u4"]
+    inp = Inputs(wl)
+    sess = make_session(gpu_lib, wl, rope="interleaved")
+    views = run(sess, inp)
+    torch.cuda.synchronize()
+    check_sampled(views, inp, wl.rank, sample_tokens(wl, n=24), "h56_u4:interleaved",
+                  rope="interleaved")
 
 
 def test_tiny_workload_full(gpu_lib):
