@@ -18,4 +18,6 @@ from .qkvx_oracle import (  # noqa: F401
     rope_rotate_half, rope_interleaved, front_end_values, front_end_rows,
     receive_slots, scatter_heads, pack_qkv_head_chunk_payload,
     pack_qkv_head_chunk_into, merge_output_head_chunk, POISON_BITS,
+    gather_heads, exchange_chunks, pack_output_sequence_chunk_payload,
+    pack_output_sequence_chunk_into, gather_output_head_chunk,
 )

@@ -389,6 +389,123 @@ def test_merge_band_form_matches_gather_heads():
     assert np.array_equal(out, ref)
 
 
+def _patterns_u16(rng, shape):
+    return rng.integers(0, 65536, shape, dtype=np.uint64).astype(np.uint16)
+
+
+def test_gather_heads_is_all_to_all():
+    """gather_heads equals the textbook all-to-all: rank r takes sequence segment
+    r of every rank's band and stacks them on the head axis in rank order."""
+    rng = np.random.default_rng(3)
+    U, B, S, HL, D = 4, 2, 3, 2, 5
+    bands = [rng.integers(0, 1000, (B, U * S, HL, D)) for _ in range(U)]
+    got = O.gather_heads(bands, U)
+    t = np.stack(bands).reshape(U, B, U, S, HL, D)            # [src, B, dst, S, hl, D]
+    ref = t.transpose(2, 1, 3, 0, 4, 5).reshape(U, B, S, U * HL, D)
+    for r in range(U):
+        assert np.array_equal(got[r], ref[r])
+
+
+@pytest.mark.parametrize("world", [1, 2, 4, 8])
+def test_gather_heads_inverts_scatter_heads(world):
+    rng = np.random.default_rng(world)
+    B, S, H, D = 2, 3, 8, 4
+    shards = [_patterns_u16(rng, (B, S, H, D)) for _ in range(world)]
+    back = O.gather_heads(O.scatter_heads(shards, world), world)
+    assert all(np.array_equal(a, b) for a, b in zip(back, shards))
+    bands = [_patterns_u16(rng, (B, world * S, H // world, D)) for _ in range(world)]
+    again = O.scatter_heads(O.gather_heads(bands, world), world)
+    assert all(np.array_equal(a, b) for a, b in zip(again, bands))
+    if world == 1:
+        assert np.array_equal(O.gather_heads(bands, 1)[0], bands[0])
+
+
+@pytest.mark.parametrize("world", [1, 2, 3, 8])
+def test_exchange_chunks_is_transpose_and_involution(world):
+    """Chunk r of rank u lands in slot u of rank r: stacking the inputs as
+    [sender, receiver, C], the outputs are the axis swap; exchanging twice gives
+    the inputs back; one rank is the identity."""
+    rng = np.random.default_rng(11)
+    C = 7
+    chunks = [rng.integers(0, 256, (world, C), dtype=np.uint64).astype(np.uint8)
+              for _ in range(world)]
+    got = O.exchange_chunks(chunks, world)
+    ref = np.swapaxes(np.stack(chunks), 0, 1)
+    for r in range(world):
+        assert np.array_equal(got[r], ref[r])
+        for u in range(world):                       # brute force, element by element
+            for i in range(C):
+                assert got[r][u, i] == chunks[u][r, i]
+    back = O.exchange_chunks(got, world)
+    assert all(np.array_equal(a, b) for a, b in zip(back, chunks))
+
+
+def test_output_sequence_payload_brute_force():
+    """Segment u of the payload holds sequence rows u*S_local + s of the band."""
+    rng = np.random.default_rng(5)
+    U, B, S, HC, D = 3, 2, 4, 2, 3
+    band = rng.integers(0, 1000, (B, U * S, HC, D))
+    p = O.pack_output_sequence_chunk_payload(band, U)
+    assert p.shape == (U, B, S, HC, D)
+    for u in range(U):
+        for b in range(B):
+            for s in range(S):
+                for j in range(HC):
+                    for e in range(D):
+                        assert p[u, b, s, j, e] == band[b, u * S + s, j, e]
+    assert np.array_equal(O.pack_output_sequence_chunk_payload(band, 1)[0], band)
+    dests = [np.full((B, S + 2, HC + 3, D), -1) for _ in range(U)]
+    O.pack_output_sequence_chunk_into(band, U, dests, 1, 2)
+    for u in range(U):
+        assert np.array_equal(dests[u][:, 1:1 + S, 2:2 + HC], p[u])
+        mask = np.ones(dests[u].shape, bool)
+        mask[:, 1:1 + S, 2:2 + HC] = False
+        assert np.all(dests[u][mask] == -1)
+
+
+@pytest.mark.parametrize("world,counts", [(4, [2, 10, 2]), (2, [7, 14, 7]), (1, [1, 2])])
+def test_output_chunks_reconstruct_gather_heads(world, counts):
+    """Running gather_output_head_chunk for every band of a complete schedule
+    rebuilds the whole-band gather_heads result ([FI-comm] class method: the
+    chunked calls reconstruct ordinary whole-head output communication); each
+    call writes only its band."""
+    rng = np.random.default_rng(21)
+    hl = sum(counts)
+    B, S, D = 2, 3, 4
+    bands = [_patterns_u16(rng, (B, world * S, hl, D)) for _ in range(world)]
+    outs = [np.full((B, S, world * hl, D), 9, np.uint16) for _ in range(world)]
+    for off, cnt in W.schedule_pairs(counts):
+        before = [o.copy() for o in outs]
+        O.gather_output_head_chunk([b[:, :, off:off + cnt] for b in bands], world, hl, off, outs)
+        band_mask = np.zeros(world * hl, bool)
+        for u in range(world):
+            band_mask[u * hl + off:u * hl + off + cnt] = True
+        for o, b0 in zip(outs, before):
+            assert np.array_equal(o[:, :, ~band_mask], b0[:, :, ~band_mask])
+    ref = O.gather_heads(bands, world)
+    assert all(np.array_equal(a, b) for a, b in zip(outs, ref))
+
+
+def test_input_and_output_chunk_paths_compose_to_identity():
+    """Input side (QKV pack into receive slots) followed by an identity
+    'attention' on V and the output side (sequence pack, exchange, merge) returns
+    every rank's own V: the two halves of the schedule are inverse maps."""
+    rng = np.random.default_rng(33)
+    world, counts, B, S, D = 4, [2, 3, 1], 1, 3, 128
+    hl = sum(counts)
+    H = world * hl
+    ranks = [tuple(_patterns_u16(rng, (B, S, H, D)) for _ in range(3)) for _ in range(world)]
+    outs = [np.zeros((B, S, H, D), np.uint16) for _ in range(world)]
+    for off, cnt in W.schedule_pairs(counts):
+        slots = [np.zeros((B, world * S, cnt, 3 * D), np.uint16) for _ in range(world)]
+        for r in range(world):
+            O.pack_qkv_head_chunk_into(*ranks[r], world, off, cnt, slots, r * S)
+        v_bands = [sl[..., 2 * D:] for sl in slots]                  # attention := V
+        O.gather_output_head_chunk(v_bands, world, hl, off, outs)
+    for r in range(world):
+        assert np.array_equal(outs[r], ranks[r][2])
+
+
 # ---------------------------------------------------------------------------
 # values printed on the pages
 # ---------------------------------------------------------------------------
