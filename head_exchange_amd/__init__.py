@@ -26,7 +26,9 @@ STATUS = {0: "OK", -1: "INVALID", -2: "DIVISIBILITY", -3: "CAPACITY", -4: "ALIGN
 # every symbol include/qkvx.h declares
 EXPORTS = ("qkvx_last_error", "qkvx_slot_bytes", "qkvx_create", "qkvx_forward",
            "qkvx_last_outputs", "qkvx_poison_receive_slots", "qkvx_describe",
-           "qkvx_destroy", "ulysses_pack_qkv_head_chunk", "ulysses_merge_output_head_chunk")
+           "qkvx_destroy", "ulysses_pack_qkv_head_chunk", "ulysses_merge_output_head_chunk",
+           "ulysses_scatter_heads", "ulysses_gather_heads", "ulysses_pack_output_sequence_chunk",
+           "ulysses_exchange_chunks")
 
 
 class QkvxError(RuntimeError):
@@ -101,6 +103,13 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.ulysses_merge_output_head_chunk.restype = i32
     lib.ulysses_merge_output_head_chunk.argtypes = [
         ctypes.POINTER(Peers), i32, i32, ctypes.POINTER(ctypes.c_int), i32, i32, vp, i32, i32, vp]
+    for name in ("ulysses_scatter_heads", "ulysses_gather_heads",
+                 "ulysses_pack_output_sequence_chunk"):
+        fn = getattr(lib, name)
+        fn.restype = i32
+        fn.argtypes = [ctypes.POINTER(View4), i32, ctypes.POINTER(Peers), vp]
+    lib.ulysses_exchange_chunks.restype = i32
+    lib.ulysses_exchange_chunks.argtypes = [vp, i32, i64, i32, ctypes.POINTER(vp), vp]
     _lib = lib
     return lib
 
@@ -317,3 +326,53 @@ def ulysses_merge_output_head_chunk(src: Sequence, *, world: int, local_heads: i
                                                   chunk, out.data_ptr(), out.shape[0],
                                                   out.shape[1], _stream(stream)))
     return out
+
+
+# ---------------------------------------------------------------------------
+# whole-band transforms and the output side (send half of one rank; the
+# destinations stand in for the peers' buffers)
+# ---------------------------------------------------------------------------
+
+def _band_to_peers(fn_name: str, x, world: int, dst: Sequence, row_offset: int,
+                   head_offset: int, stream) -> None:
+    vx = view4(x)
+    pd = peers(dst, row_offset, head_offset)
+    _check(getattr(load(), fn_name)(ctypes.byref(vx), world, ctypes.byref(pd), _stream(stream)))
+
+
+def ulysses_scatter_heads(x, *, world: int, dst: Sequence, row_offset: int = 0,
+                          head_offset: int = 0, stream=None) -> None:
+    """x [B, S_local, H, 128]: head slice d goes to ``dst[d]`` ([B, rows, heads,
+    128]) at rows ``row_offset..`` and heads ``head_offset..``."""
+    _band_to_peers("ulysses_scatter_heads", x, world, dst, row_offset, head_offset, stream)
+
+
+def ulysses_gather_heads(x, *, world: int, dst: Sequence, row_offset: int = 0,
+                         head_offset: int = 0, stream=None) -> None:
+    """x [B, S_global, H_local, 128]: sequence segment u goes to ``dst[u]``
+    ([B, rows, heads, 128]) at rows ``row_offset..`` and heads ``head_offset..``."""
+    _band_to_peers("ulysses_gather_heads", x, world, dst, row_offset, head_offset, stream)
+
+
+def ulysses_pack_output_sequence_chunk(x, *, world: int, dst: Sequence, row_offset: int = 0,
+                                       head_offset: int = 0, stream=None) -> None:
+    """x [B, S_global, head_count, 128] (one attention-output head band): sequence
+    segment u goes to ``dst[u]`` at rows ``row_offset..``, heads ``head_offset..``."""
+    _band_to_peers("ulysses_pack_output_sequence_chunk", x, world, dst, row_offset, head_offset,
+                   stream)
+
+
+def ulysses_exchange_chunks(x, *, world: int, rank: int, dst: Sequence, stream=None) -> None:
+    """x: contiguous [..., world, chunk] tensor of any dtype; chunk u goes to
+    ``dst[u]`` (same shape and dtype) at slot ``rank``."""
+    if not x.is_contiguous() or x.shape[-2] != world:
+        raise ValueError("x must be a contiguous [..., world, chunk] tensor")
+    chunk_bytes = x.numel() * x.element_size() // world
+    for t in dst:
+        if t.dtype != x.dtype or tuple(t.shape) != tuple(x.shape) or not t.is_contiguous():
+            raise ValueError("every destination must be contiguous with x's shape and dtype")
+    if len(dst) != world:
+        raise ValueError(f"expected {world} destinations, got {len(dst)}")
+    ptrs = (ctypes.c_void_p * world)(*[t.data_ptr() for t in dst])
+    _check(load().ulysses_exchange_chunks(x.data_ptr(), world, chunk_bytes, rank, ptrs,
+                                          _stream(stream)))

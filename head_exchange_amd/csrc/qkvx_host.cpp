@@ -493,23 +493,129 @@ int ulysses_merge_output_head_chunk(const qkvx_peers* src, int world, int local_
     for (int u = 0; u < world; ++u)
         if (overlap(orng, peers_touched(src, u, batch, s_local, hc, QKVX_HEAD_DIM)))
             return fail(QKVX_ERR_ALIAS, "src.base[%d] overlaps out", u);
-    MergeArgs a;
+    BandCopyArgs a;
     memset(&a, 0, sizeof(a));
-    a.out = static_cast<uint16_t*>(out) + int64_t(off) * 128;
-    a.ob = int64_t(s_local) * H * 128;
-    a.os = H * 128;
     a.sb = src->stride[0];
     a.ss = src->stride[1];
     a.sh = src->stride[2];
+    a.db = int64_t(s_local) * H * 128;
+    a.ds = H * 128;
+    a.dh = 128;
     a.total = uint32_t(total);
-    a.local_heads = local_heads;
     a.div_hc = FastDiv(uint32_t(hc));
     a.div_s = FastDiv(uint32_t(s_local));
-    for (int u = 0; u < world; ++u)
+    for (int u = 0; u < world; ++u) {
         a.src[u] = static_cast<const uint16_t*>(src->base[u]) + src->row_offset * src->stride[1] +
                    src->head_offset * src->stride[2];
-    hipError_t e = launch_merge(a, world, static_cast<hipStream_t>(stream));
+        a.dst[u] = static_cast<uint16_t*>(out) + (int64_t(u) * local_heads + off) * 128;
+    }
+    hipError_t e = launch_band_copy(a, world, static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return hip_fail(e, "merge launch");
+    return ok();
+}
+
+// Shared by ulysses_scatter_heads, ulysses_gather_heads and
+// ulysses_pack_output_sequence_chunk: validates x and dst, then copies a
+// [B, S_local, head_count] block of head vectors per peer y from
+// x + y*peer_step (peer_step = H_local head strides or S_local row strides).
+static int band_to_peers(const qkvx_view4* x, int world, const qkvx_peers* dst, bool split_heads,
+                         void* stream, const char* what) {
+    int st = check_view(x, "x");
+    if (st) return st;
+    if (world < 1 || world > QKVX_MAX_WORLD)
+        return fail(QKVX_ERR_INVALID, "world %d outside [1, %d]", world, QKVX_MAX_WORLD);
+    const int64_t B = x->shape[0];
+    int64_t S, HC, step;
+    if (split_heads) {
+        if (x->shape[2] % world)
+            return fail(QKVX_ERR_DIVISIBILITY, "H = %lld is not divisible by world %d",
+                        (long long)x->shape[2], world);
+        S = x->shape[1];
+        HC = x->shape[2] / world;
+        step = HC * x->stride[2];
+    } else {
+        if (x->shape[1] % world)
+            return fail(QKVX_ERR_DIVISIBILITY, "S_global = %lld is not divisible by world %d",
+                        (long long)x->shape[1], world);
+        S = x->shape[1] / world;
+        HC = x->shape[2];
+        step = S * x->stride[1];
+    }
+    st = check_peers(dst, "dst", world, B, S, int(HC), QKVX_HEAD_DIM);
+    if (st) return st;
+    const int64_t total = B * S * HC * 16;
+    if (total >= kInt32Limit)
+        return fail(QKVX_ERR_INT32_RANGE, "%lld vectors per peer exceed 2^31", (long long)total);
+    const Range xr = view_range(x->base, x->shape, x->stride, 4);
+    for (int u = 0; u < world; ++u)
+        if (overlap(xr, peers_touched(dst, u, B, S, int(HC), QKVX_HEAD_DIM)))
+            return fail(QKVX_ERR_ALIAS, "dst.base[%d] overlaps x", u);
+    BandCopyArgs a;
+    memset(&a, 0, sizeof(a));
+    a.sb = x->stride[0];
+    a.ss = x->stride[1];
+    a.sh = x->stride[2];
+    a.db = dst->stride[0];
+    a.ds = dst->stride[1];
+    a.dh = dst->stride[2];
+    a.total = uint32_t(total);
+    a.div_hc = FastDiv(uint32_t(HC));
+    a.div_s = FastDiv(uint32_t(S));
+    for (int u = 0; u < world; ++u) {
+        a.src[u] = static_cast<const uint16_t*>(x->base) + int64_t(u) * step;
+        a.dst[u] = static_cast<uint16_t*>(dst->base[u]) + dst->row_offset * dst->stride[1] +
+                   dst->head_offset * dst->stride[2];
+    }
+    hipError_t e = launch_band_copy(a, world, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, what);
+    return ok();
+}
+
+int ulysses_scatter_heads(const qkvx_view4* x, int world, const qkvx_peers* dst, void* stream) {
+    return band_to_peers(x, world, dst, true, stream, "scatter_heads launch");
+}
+
+int ulysses_gather_heads(const qkvx_view4* x, int world, const qkvx_peers* dst, void* stream) {
+    return band_to_peers(x, world, dst, false, stream, "gather_heads launch");
+}
+
+int ulysses_pack_output_sequence_chunk(const qkvx_view4* x, int world, const qkvx_peers* dst,
+                                       void* stream) {
+    return band_to_peers(x, world, dst, false, stream, "output sequence pack launch");
+}
+
+int ulysses_exchange_chunks(const void* x, int world, int64_t chunk_bytes, int rank,
+                            void* const* dst, void* stream) {
+    if (!x) return fail(QKVX_ERR_INVALID, "x is NULL");
+    if (!dst) return fail(QKVX_ERR_INVALID, "dst is NULL");
+    if (world < 1 || world > QKVX_MAX_WORLD)
+        return fail(QKVX_ERR_INVALID, "world %d outside [1, %d]", world, QKVX_MAX_WORLD);
+    if (rank < 0 || rank >= world)
+        return fail(QKVX_ERR_INVALID, "rank %d outside [0, %d)", rank, world);
+    if (chunk_bytes < 1)
+        return fail(QKVX_ERR_INVALID, "chunk_bytes %lld must be >= 1", (long long)chunk_bytes);
+    bool vec16 = (chunk_bytes % 16) == 0 && aligned16(x);
+    for (int u = 0; u < world; ++u) {
+        if (!dst[u]) return fail(QKVX_ERR_INVALID, "dst[%d] is NULL", u);
+        vec16 = vec16 && aligned16(dst[u]);
+    }
+    const int64_t items = vec16 ? chunk_bytes / 16 : chunk_bytes;
+    if (items >= kInt32Limit)
+        return fail(QKVX_ERR_INT32_RANGE, "chunk of %lld bytes exceeds the per-peer limit",
+                    (long long)chunk_bytes);
+    const Range xr = bytes_range(x, chunk_bytes * world);
+    for (int u = 0; u < world; ++u)
+        if (overlap(xr, bytes_range(static_cast<uint8_t*>(dst[u]) + int64_t(rank) * chunk_bytes,
+                                    chunk_bytes)))
+            return fail(QKVX_ERR_ALIAS, "dst[%d] overlaps x", u);
+    ChunkArgs a;
+    memset(&a, 0, sizeof(a));
+    a.src = static_cast<const uint8_t*>(x);
+    a.chunk = chunk_bytes;
+    for (int u = 0; u < world; ++u)
+        a.dst[u] = static_cast<uint8_t*>(dst[u]) + int64_t(rank) * chunk_bytes;
+    hipError_t e = launch_chunks(a, world, vec16, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "exchange_chunks launch");
     return ok();
 }
 

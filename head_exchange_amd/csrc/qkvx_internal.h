@@ -79,20 +79,34 @@ struct PackArgs {
     uint16_t* dst[QKVX_MAX_WORLD]; // peer d at [0, row_offset, head_offset, 0]
 };
 
-struct MergeArgs {
-    uint16_t* out;                 // [B, S, world*local_heads, 128] at head off
-    int64_t ob, os;                // out strides (b, s); head stride is 128
-    int64_t sb, ss, sh;            // source strides (b, row, head)
-    uint32_t total;                // 16-byte chunks per source
-    int32_t local_heads;
+// A per-peer strided copy of 128-element head vectors: for peer y (< world),
+// band head j (< head_count) and token (b, s) of [B, S]:
+//   dst[y][b*db + s*ds + j*dh + e] = src[y][b*sb + s*ss + j*sh + e]
+// Merge, whole-band scatter/gather and the output sequence split are all this
+// map with different peer base pointers.
+struct BandCopyArgs {
+    int64_t sb, ss, sh;            // source strides (b, s, head)
+    int64_t db, ds, dh;            // destination strides (b, s, head)
+    uint32_t total;                // 16-byte chunks per peer: B*S*head_count*16
     FastDiv div_hc, div_s;
-    const uint16_t* src[QKVX_MAX_WORLD];  // peer u at [0, row_offset, head_offset, 0]
+    const uint16_t* src[QKVX_MAX_WORLD];
+    uint16_t* dst[QKVX_MAX_WORLD];
+};
+
+// Equal-length byte chunks: peer y receives bytes [y*chunk, (y+1)*chunk) of src
+// at dst[y] (already offset to the sender's slot).
+struct ChunkArgs {
+    const uint8_t* src;
+    int64_t chunk;                 // bytes per peer
+    uint8_t* dst[QKVX_MAX_WORLD];
 };
 
 // Launchers (enqueue only; arguments already validated).
 hipError_t launch_fused(const FusedArgs& a, hipStream_t stream);
 hipError_t launch_pack(const PackArgs& a, int world, hipStream_t stream);
-hipError_t launch_merge(const MergeArgs& a, int world, hipStream_t stream);
+hipError_t launch_band_copy(const BandCopyArgs& a, int world, hipStream_t stream);
+// vec16: chunk and every address are multiples of 16 bytes
+hipError_t launch_chunks(const ChunkArgs& a, int world, bool vec16, hipStream_t stream);
 hipError_t launch_fill16(uint16_t* p, int64_t n, uint16_t value, hipStream_t stream);
 
 // Tile plan of the fused kernel (exposed for describe()).

@@ -1,15 +1,19 @@
-// Head-chunk pack and merge kernels for gfx950.
+// Transport kernels for gfx950: the head-chunk pack, the per-peer band copy
+// (merge, whole-band scatter/gather, output sequence split) and the byte-chunk
+// exchange.
 //
-// Both are bit copies between strided bf16 tensors whose innermost axis is one
-// 128-element (256-byte) head vector, so every access is a 16-byte vector and a
-// group of 16 lanes moves one whole head: a wave touches four 256-byte runs per
-// instruction on each side, i.e. whole 128-byte cache lines.  Reading the pages'
-// index maps ("Head-Chunk Layout and Transport Primitives" on
-// docs.flashinfer.ai/api/comm.html):
-//   pack : dst_d[b, R0 + s, j, p*128 + e] = part_p[b, s, d*H_local + off + j, e]
-//   merge: out[b, s, u*H_local + off + j, e] = src_u[b, R0 + s, j0 + j, e]
-// The peer index (d or u) is blockIdx.y, so the peer's base pointer is a
-// wave-uniform kernel argument and no per-lane table lookup is needed; the rest
+// All head-vector kernels are bit copies between strided bf16 tensors whose
+// innermost axis is one 128-element (256-byte) head vector, so every access is
+// a 16-byte vector and a group of 16 lanes moves one whole head: a wave touches
+// four 256-byte runs per instruction on each side, i.e. whole 128-byte cache
+// lines.  Index maps ("Head-Chunk Layout and Transport Primitives" and "Ulysses
+// Context-Parallel All-to-All" on docs.flashinfer.ai/api/comm.html):
+//   pack   : dst_d[b, R0 + s, j, p*128 + e] = part_p[b, s, d*H_local + off + j, e]
+//   merge  : out[b, s, u*H_local + off + j, e] = src_u[b, R0 + s, j0 + j, e]
+//   scatter: dst_d[b, R0 + s, j0 + j, e] = x[b, s, d*H_local + j, e]
+//   gather : dst_u[b, R0 + s, j0 + j, e] = x[b, u*S_local + s, j, e]
+// The peer index (d or u) is blockIdx.y, so the peer's base pointers are
+// wave-uniform kernel arguments and no per-lane table lookup is needed; the rest
 // of the flat 16-byte-chunk index is split with precomputed 32-bit dividers.
 // Each thread moves one 16-byte vector with nontemporal accesses.
 #include "qkvx_internal.h"
@@ -51,17 +55,35 @@ __global__ __launch_bounds__(kThreads) void pack_kernel(PackArgs a) {
     store_nt(dst, load_nt(src));
 }
 
-__global__ __launch_bounds__(kThreads) void merge_kernel(MergeArgs a) {
-    const uint32_t u = blockIdx.y;
+__global__ __launch_bounds__(kThreads) void band_copy_kernel(BandCopyArgs a) {
+    const uint32_t y = blockIdx.y;
     const uint32_t c = blockIdx.x * kThreads + threadIdx.x;
     if (c >= a.total) return;
     const uint32_t e16 = c & 15u;
     uint32_t tok, j, b, s;
     a.div_hc.divmod(c >> 4, tok, j);
     a.div_s.divmod(tok, b, s);
-    const uint16_t* src = a.src[u] + b * a.sb + s * a.ss + j * a.sh + e16 * 8;
-    uint16_t* out = a.out + int64_t(u) * a.local_heads * 128 + b * a.ob + s * a.os + j * 128 + e16 * 8;
-    store_nt(out, load_nt(src));
+    const uint16_t* src = a.src[y] + b * a.sb + s * a.ss + j * a.sh + e16 * 8;
+    uint16_t* dst = a.dst[y] + b * a.db + s * a.ds + j * a.dh + e16 * 8;
+    store_nt(dst, load_nt(src));
+}
+
+// Byte chunks, 16 bytes per thread (chunk and addresses 16-byte aligned).
+__global__ __launch_bounds__(kThreads) void chunk16_kernel(ChunkArgs a) {
+    const uint32_t y = blockIdx.y;
+    const int64_t i = (int64_t(blockIdx.x) * kThreads + threadIdx.x) * 16;
+    if (i >= a.chunk) return;
+    const u32x4 v = __builtin_nontemporal_load(
+        reinterpret_cast<const u32x4*>(a.src + int64_t(y) * a.chunk + i));
+    __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(a.dst[y] + i));
+}
+
+// Byte chunks of any length and alignment, one byte per thread.
+__global__ __launch_bounds__(kThreads) void chunk1_kernel(ChunkArgs a) {
+    const uint32_t y = blockIdx.y;
+    const int64_t i = int64_t(blockIdx.x) * kThreads + threadIdx.x;
+    if (i >= a.chunk) return;
+    a.dst[y][i] = a.src[int64_t(y) * a.chunk + i];
 }
 
 __global__ __launch_bounds__(kThreads) void fill16_kernel(uint16_t* p, int64_t n, uint32_t pattern) {
@@ -85,11 +107,22 @@ hipError_t launch_pack(const PackArgs& a, int world, hipStream_t stream) {
     return hipGetLastError();
 }
 
-hipError_t launch_merge(const MergeArgs& a, int world, hipStream_t stream) {
+hipError_t launch_band_copy(const BandCopyArgs& a, int world, hipStream_t stream) {
     if (a.total == 0) return hipSuccess;
-    const uint32_t per_block = kThreads;
-    dim3 grid((a.total + per_block - 1) / per_block, world);
-    hipLaunchKernelGGL(merge_kernel, grid, dim3(kThreads), 0, stream, a);
+    dim3 grid((a.total + kThreads - 1) / kThreads, world);
+    hipLaunchKernelGGL(band_copy_kernel, grid, dim3(kThreads), 0, stream, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_chunks(const ChunkArgs& a, int world, bool vec16, hipStream_t stream) {
+    if (a.chunk == 0) return hipSuccess;
+    const int64_t per_thread = vec16 ? 16 : 1;
+    const int64_t items = (a.chunk + per_thread - 1) / per_thread;
+    dim3 grid(uint32_t((items + kThreads - 1) / kThreads), world);
+    if (vec16)
+        hipLaunchKernelGGL(chunk16_kernel, grid, dim3(kThreads), 0, stream, a);
+    else
+        hipLaunchKernelGGL(chunk1_kernel, grid, dim3(kThreads), 0, stream, a);
     return hipGetLastError();
 }
 

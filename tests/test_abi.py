@@ -249,6 +249,74 @@ def test_merge_rejects(lib, kw, status):
     assert merge(lib, src, **args) == status, lib.qkvx_last_error()
 
 
+BAND_SHAPE = [1, 64, 8, 128]          # scatter: [B, S_local, H, 128]; gather: [B, S_global, H_local, 128]
+
+
+def band_call(lib, name, x, world, dst):
+    return getattr(lib, name)(ctypes.byref(x), world, ctypes.byref(dst), None)
+
+
+@pytest.mark.parametrize("name", ["ulysses_scatter_heads", "ulysses_gather_heads",
+                                  "ulysses_pack_output_sequence_chunk"])
+@pytest.mark.parametrize("mutate,status", [
+    (lambda a: a.update(world=3), -2),                       # 8 heads / 64 rows % 3
+    (lambda a: a.update(world=0), -1),
+    (lambda a: a.update(world=65), -1),
+    (lambda a: a["x"].shape.__setitem__(3, 64), -1),
+    (lambda a: a["x"].stride.__setitem__(3, 2), -7),
+    (lambda a: a["x"].stride.__setitem__(0, -8), -7),
+    (lambda a: setattr(a["x"], "base", FAKE + 2), -4),
+    (lambda a: a["x"].stride.__setitem__(1, 1028), -4),
+    (lambda a: setattr(a["dst"], "world", 4), -1),
+    (lambda a: setattr(a["dst"], "row_offset", 120), -3),
+    (lambda a: setattr(a["dst"], "heads", 3), -3),
+    (lambda a: a["dst"].stride.__setitem__(2, 64), -7),
+    (lambda a: a["dst"].base.__setitem__(1, SRC[0] + 4096), -5),   # lands inside x
+    (lambda a: a["dst"].base.__setitem__(0, 0), -1),
+    (lambda a: a["dst"].base.__setitem__(0, DST[0] + 8), -4),
+])
+def test_band_transforms_reject(lib, name, mutate, status):
+    x = view(SRC[0], BAND_SHAPE, contiguous(BAND_SHAPE))
+    # generous peers: 128 rows, 8 heads fit every form of the three calls at world 2
+    dst = peers(DST, 1, 128, 8, 128)
+    a = dict(x=x, world=2, dst=dst)
+    mutate(a)
+    assert band_call(lib, name, a["x"], a["world"], a["dst"]) == status, lib.qkvx_last_error()
+
+
+def test_band_transforms_reject_int32_overflow(lib):
+    shape = [1, 1 << 20, 64, 128]
+    x = view(SRC[0], shape, contiguous(shape))
+    dst = peers(DST, 1, 1 << 21, 32, 128)
+    assert band_call(lib, "ulysses_scatter_heads", x, 2, dst) == -6
+
+
+def exchange(lib, x, world, chunk, rank, dsts):
+    arr = (ctypes.c_void_p * len(dsts))(*dsts)
+    return lib.ulysses_exchange_chunks(ctypes.c_void_p(x), world, chunk, rank, arr, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(x=0), -1),
+    (dict(rank=2), -1),
+    (dict(rank=-1), -1),
+    (dict(world=0), -1),
+    (dict(chunk=0), -1),
+    (dict(dsts=[DST[0], 0]), -1),
+    (dict(dsts=[DST[0], SRC[0]]), -5),         # slot 0 of peer 1 is x itself
+    (dict(chunk=1 << 31, x=FAKE + 1), -6),     # byte path: 2^31 items
+])
+def test_exchange_rejects(lib, kw, status):
+    args = dict(x=SRC[0], world=2, chunk=4096, rank=0, dsts=list(DST))
+    args.update(kw)
+    assert exchange(lib, args["x"], args["world"], args["chunk"], args["rank"],
+                    args["dsts"]) == status, lib.qkvx_last_error()
+
+
+def test_exchange_rejects_null_array(lib):
+    assert lib.ulysses_exchange_chunks(ctypes.c_void_p(SRC[0]), 2, 16, 0, None, None) == -1
+
+
 def test_python_binding_fails_loudly_without_library(tmp_path):
     import importlib
     mod = importlib.reload(hx)

@@ -15,7 +15,10 @@ float64, the draw is rounded to float32, and bf16 tensors are then rounded to
 bf16 with round-to-nearest-even.  Seeds are ``20261202 + 100*config + tensor_id``
 with tensor ids x=1, W=2, q-norm weight=3, k-norm weight=4, q=5, k=6, v=7,
 merge band=8, fused qkv source=9; call i of a multi-call workload adds 10*i to the
-seed of x.  ``N(0, a)`` means standard deviation ``a``.
+seed of x.  ``N(0, a)`` means standard deviation ``a``.  The whole-band
+transforms simulate every rank of a group; rank r's tensors use ids shard=50
+([B, S_local, H, 128]), output band=60 ([B, S_global, head_count, 128]) and
+byte chunks=70 (uniform bytes, [world, C]), plus 100000*r.
 
 The cos/sin table is an input of the operation (a per-token [rows, 128] fp32
 table): row ``p`` holds ``cos(p*theta_i)`` in columns ``i < 64`` and
@@ -33,7 +36,8 @@ import torch
 HEAD_DIM = 128
 SEED_BASE = 20261202
 TENSOR_IDS = {"x": 1, "w": 2, "wq": 3, "wk": 4, "q": 5, "k": 6, "v": 7,
-              "band": 8, "qkv384": 9}
+              "band": 8, "qkv384": 9, "shard": 50, "oband": 60, "chunks": 70}
+RANK_SEED_STEP = 100000
 
 
 @dataclass(frozen=True)
@@ -82,8 +86,8 @@ class Workload:
         """(M, N, K) of the QKV projection."""
         return self.tokens, 3 * self.hidden, self.hidden
 
-    def seed(self, tensor: str, call: int = 0) -> int:
-        s = SEED_BASE + 100 * self.index + TENSOR_IDS[tensor]
+    def seed(self, tensor: str, call: int = 0, rank: int = 0) -> int:
+        s = SEED_BASE + 100 * self.index + TENSOR_IDS[tensor] + RANK_SEED_STEP * rank
         if tensor == "x":
             s += 10 * call
         return s
@@ -200,6 +204,29 @@ def merge_band(w: Workload) -> np.ndarray:
     """Seeded attention-output band [B, S_global, H_local, 128] (bf16 bits)."""
     return normal_bf16(w.seed("band"),
                        (w.batch, w.s_global, w.local_heads, w.head_dim), 1.0)
+
+
+def rank_shards(w: Workload) -> list:
+    """Every rank's [B, S_local, H, 128] input of scatter_heads (bf16 bits)."""
+    shape = (w.batch, w.s_local, w.heads, w.head_dim)
+    return [normal_bf16(w.seed("shard", rank=r), shape, 1.0) for r in range(w.world)]
+
+
+def rank_bands(w: Workload, head_count: int | None = None, ranks=None) -> list:
+    """Every rank's (or the listed ranks') attention-output band
+    [B, S_global, head_count, 128] (head_count defaults to H_local: the whole
+    band of gather_heads)."""
+    hc = w.local_heads if head_count is None else head_count
+    shape = (w.batch, w.s_global, hc, w.head_dim)
+    ranks = range(w.world) if ranks is None else ranks
+    return [normal_bf16(w.seed("oband", rank=r), shape, 1.0) for r in ranks]
+
+
+def rank_chunks(w: Workload, chunk_bytes: int) -> list:
+    """Every rank's [world, chunk_bytes] byte payload of exchange_chunks."""
+    return [_rng(w.seed("chunks", rank=r)).integers(0, 256, (w.world, chunk_bytes),
+                                                    dtype=np.uint8)
+            for r in range(w.world)]
 
 
 def schedule_pairs(counts) -> Tuple[Tuple[int, int], ...]:
