@@ -121,6 +121,56 @@ def cpu_baseline(wl, x, w, wq, wk, cs, qkv_src, band, target_s: float):
             "seconds": round(dt, 2), "tokens": T}
 
 
+def output_side(hx, torch, wl, band, sched, dev, reps: int = 10):
+    """Times the whole-band and output-side transforms of one rank on the same
+    shard (outside the step): scatter_heads of a [B, S_local, H, 128] input,
+    gather_heads of the [B, S_global, H_local, 128] band, the output sequence
+    split of every chunk into contiguous staging, and exchange_chunks of the
+    whole-band Q|K|V message (B*S_local*H_local*384 bf16 per peer).  Bytes are
+    algorithmic: every element read once and written once."""
+    S, U, hl, B = wl.s_local, wl.world, wl.local_heads, wl.batch
+    stream = torch.cuda.current_stream()
+    shard = torch.empty(B, S, wl.heads, 128, dtype=torch.bfloat16, device=dev).normal_()
+    scat = [torch.empty(B, wl.s_global, hl, 128, dtype=torch.bfloat16, device=dev)
+            for _ in range(U)]
+    gath = [torch.empty(B, S, wl.heads, 128, dtype=torch.bfloat16, device=dev) for _ in range(U)]
+    staging = [torch.empty(U, B, S, cnt, 128, dtype=torch.bfloat16, device=dev)
+               for _, cnt in sched]
+    msg = B * S * hl * 384 * 2
+    ex_x = torch.empty(U, msg, dtype=torch.uint8, device=dev).random_(0, 256)
+    ex_out = [torch.empty(U, msg, dtype=torch.uint8, device=dev) for _ in range(U)]
+    cases = {
+        "scatter_heads": (lambda: hx.ulysses_scatter_heads(shard, world=U, dst=scat,
+                                                           row_offset=wl.rank * S, stream=stream),
+                          2.0 * shard.numel() * 2),
+        "gather_heads": (lambda: hx.ulysses_gather_heads(band, world=U, dst=gath,
+                                                         head_offset=wl.rank * hl, stream=stream),
+                         2.0 * band.numel() * 2),
+        "output_sequence_pack_all_chunks": (
+            lambda: [hx.ulysses_pack_output_sequence_chunk(
+                band[:, :, off:off + cnt], world=U, dst=[st[u] for u in range(U)], stream=stream)
+                for (off, cnt), st in zip(sched, staging)],
+            2.0 * band.numel() * 2),
+        "exchange_chunks": (lambda: hx.ulysses_exchange_chunks(ex_x, world=U, rank=wl.rank,
+                                                               dst=ex_out, stream=stream),
+                            2.0 * U * msg),
+    }
+    out = {}
+    for name, (fn, nbytes) in cases.items():
+        fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / reps
+        gbps = nbytes / (us * 1e-6) / 1e9
+        out[name] = {"us": us, "bytes": nbytes, "gbps": gbps, "frac": gbps / PEAK_HBM_GBPS}
+    return out
+
+
 def main():
     args = parse()
     world_env = int(os.environ.get("WORLD_SIZE", "1"))
@@ -247,6 +297,7 @@ def main():
                       "peak_gbps": PEAK_HBM_GBPS},
         "kernels_ms": {"fused": fused_ms, "pack_all_chunks": pack_ms, "merge_all_chunks": merge_ms},
     }
+    result["output_side"] = output_side(hx, torch, wl, band, sched, dev)
     if calib:
         result["copy_calibration"] = calib
     if not args.skip_cpu_baseline:

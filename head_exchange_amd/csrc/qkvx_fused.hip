@@ -1,5 +1,5 @@
-// Fused QKV projection + per-head RMSNorm(Q, K) + rotate-half RoPE + head-band
-// store, as one gfx950 kernel.
+// Fused QKV projection + per-head RMSNorm(Q, K) + RoPE + head-band store, as one
+// gfx950 kernel.
 //
 // What it computes follows the pages' fused front end (docs.flashinfer.ai/api/
 // comm.html, "Fused QKV Projection + Norm + RoPE + Head Exchange"; the QKV
@@ -14,24 +14,37 @@
 //    column (here: one token) and 16 rows (here: head dims), and lanes l and
 //    l+32 share the token.  A wave's 128-row n-range is exactly one head, so
 //    the RMS reduction over the head is a register sum plus one exchange with
-//    lane l^32, and the RoPE partners e and e+64 sit in the same lane and
-//    register of n-blocks b and b+2: the whole epilogue is lane-local.
+//    lane l^32, and both RoPE pairings keep their partners in one lane: the
+//    whole epilogue is lane-local.
 //  * Block tile 256 tokens x 256 columns (two heads), K-step 64, four waves in a
-//    2 x 2 grid, each owning 128 columns (one head) x 128 tokens: 16
-//    accumulators of 32x32 per wave (256 fp32 per lane).
-//  * Operands are K-contiguous, read with bounds-checked buffer loads (rows
-//    past M or N read as zero, so tails need no clamping), staged through a
-//    double-buffered LDS ring with an XOR swizzle of the 16-byte chunks that
-//    keeps both the chunk writes and the MFMA fragment reads free of bank
-//    conflicts.  The next K-tile's global loads are in flight while the
-//    current tile's MFMAs run.
+//    2 x 2 grid, each owning one head x 128 tokens: 16 accumulators of 32x32
+//    per wave, all 256 AGPRs of the lane.
+//  * Operands are K-contiguous and go straight from global memory to LDS
+//    (buffer_load ... lds, bounds-checked: rows past M or N read as zero),
+//    128 bytes per row per request.  How fast they arrive is set by how many
+//    requests a compute unit keeps in flight, and a wait that drains them all
+//    once per K-step leaves the memory pipeline idle for a full latency each
+//    time.  So the LDS is a ring of five 32 KB buffers, each holding the W or
+//    the X half of one K-step: while the MFMAs use K-step k (two buffers), the
+//    X half of k+1 and the W half of k+2 load into the buffers K-step k-1 used,
+//    and the wait at the end of the step leaves the W half of k+2 in flight.
+//    Within a buffer the 16-byte chunks of each 8-row block are XOR-swizzled by
+//    the block index, so the fragment reads are free of bank conflicts.
+//  * The main loop is a fixed sequence per K-step: 64 MFMA slots in four
+//    phases (each phase one 16-deep sub-step of all 16 accumulators), the next
+//    sub-step's eight fragment reads right after the first eight MFMAs of a
+//    phase, and the 16 load instructions one per three MFMAs.  MFMAs and
+//    fragment reads are written as inline assembly with explicit
+//    lgkmcnt waits: the buffer a read uses is only known at run time, and
+//    the compiler, unable to tell it from the buffers being loaded, would
+//    otherwise wait for every load in flight before each read.
 //  * Persistent: one workgroup per CU walks its share of the tiles, and the
-//    K-tiles of consecutive output tiles form one continuous load stream, so
-//    the next tile's first K-tiles are in flight while the current tile's
-//    epilogue runs.  In each round the 8 XCDs (workgroup b runs on XCD b % 8)
-//    take consecutive ranges of a tile order that walks groups of tile rows
-//    column by column, so the tiles an XCD runs together share X and W
-//    panels in its L2.
+//    K-steps of consecutive output tiles form one continuous load stream, so
+//    the next tile's first K-steps are in flight while the current tile's
+//    epilogue runs.  The 8 XCDs (workgroup b runs on XCD b % 8) take
+//    consecutive ranges of a tile order that walks groups of tile rows column
+//    by column, so the tiles an XCD runs together share X and W panels in its
+//    L2.
 #include "qkvx_internal.h"
 
 namespace qkvx {
@@ -39,36 +52,34 @@ namespace {
 
 constexpr int BM = 256;        // tokens per tile
 constexpr int BN = 256;        // output columns per tile (two heads)
-constexpr int BK = 64;         // K per LDS stage (128 bytes of each operand row)
+constexpr int BK = 64;         // K per step (128 bytes of each operand row)
 constexpr int NT = 256;        // threads: four waves
 constexpr int GROUP_M = 8;     // tile rows walked together in the tile order
 constexpr int NXCD = 8;
-constexpr int CHUNKS = BK / 8;                 // 16-byte chunks per operand row
-// LDS image of one operand stage: 32 blocks of 8 rows x 128 bytes, each block
-// followed by 16 bytes of padding (65 chunks per block).
-constexpr int BLOCK_CHUNKS = 65;
-constexpr int STAGE_CHUNKS = 32 * BLOCK_CHUNKS;   // 2080 chunks = 33280 bytes
-constexpr int LOADS = 32 / 4;                  // block loads per wave per operand per stage
+constexpr int NBUF = 5;        // ring of half-step buffers
+constexpr int BUF_CHUNKS = 2048;    // 16-byte chunks per buffer: 256 rows x 128 bytes
+constexpr int HLOADS = 8;      // load instructions per wave per half step
+constexpr int LSTEP = 3;       // MFMA slots per load instruction
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 
-// LDS chunk index of chunk c of tile row r of one operand stage: block r / 8
-// holds rows 8 (r / 8) .. + 7 as 128 contiguous bytes each, and every 1 KB block
-// is followed by 16 bytes of padding.  A direct load (64 lanes x 16 bytes into
-// 1 KB of LDS) therefore reads eight consecutive rows' 128-byte segments in
-// ascending order -- one 128-byte request each.
-__device__ __forceinline__ int lds_chunk(int r, int c) {
-    return (r >> 3) * BLOCK_CHUNKS + (r & 7) * CHUNKS + c;
+// 16-byte chunk index, within one buffer, of chunk c (0..7) of tile row r:
+// block r / 8 holds rows 8 (r / 8) .. + 7, 128 bytes each, with chunk c of a
+// row at position c ^ (block % 8).  Fragment reads of one chunk by lanes whose
+// rows lie in eight consecutive blocks therefore hit eight different 16-byte
+// bank groups.
+__device__ __forceinline__ int lds_pos(int r, int c) {
+    const int b = r >> 3;
+    return b * 64 + (r & 7) * 8 + (c ^ (b & 7));
 }
 
-// Row of a 128-row wave range that MFMA row i (0..31) of 32-row block nb maps
-// to.  Lanes i..i+7 read the same chunk of rows 8 apart, i.e. of eight
-// consecutive blocks 1040 bytes apart: distinct LDS banks (32 and 64 banks).
-__device__ __forceinline__ int mfma_row(int nb, int i) {
-    return 64 * (nb >> 1) + 8 * (i & 7) + 4 * (nb & 1) + (i >> 3);
+// Row of a wave's 128-row range that MFMA row i (0..31) of 32-row block blk
+// maps to.  Lanes i..i+7 read rows 8 apart, i.e. in eight consecutive blocks.
+__device__ __forceinline__ int mfma_row(int blk, int i) {
+    return 64 * (blk >> 1) + 8 * (i & 7) + 4 * (blk & 1) + (i >> 3);
 }
 
 // Tile coordinates of logical tile l: groups of group_m tile rows, walked
@@ -88,12 +99,24 @@ __device__ __forceinline__ uint16_t bf16_bits(float f) {
     return __builtin_bit_cast(uint16_t, static_cast<__bf16>(f));
 }
 
+// Accumulators are read with explicit v_accvgpr_read so that the compiler
+// never copies all 256 of them into VGPRs at once (there is no room).
+__device__ __forceinline__ float acc_read(const float& a) {
+    float v;
+    asm volatile("v_accvgpr_read_b32 %0, %1" : "=v"(v) : "a"(a));
+    return v;
+}
+
+template <int N>
+__device__ __forceinline__ void wait_lgkm() {
+    asm volatile("s_waitcnt lgkmcnt(%0)" ::"n"(N) : "memory");
+}
+
 __global__ __attribute__((amdgpu_flat_work_group_size(NT, NT), amdgpu_waves_per_eu(1, 1)))
 void fused_qkv_kernel(FusedArgs a) {
-    // Two LDS stages per operand, as separate objects so that the compiler can
-    // tell a direct load into one stage from fragment reads of the other.
-    __shared__ uint4 lw0[STAGE_CHUNKS], lw1[STAGE_CHUNKS];   // 33280 bytes each
-    __shared__ uint4 lx0[STAGE_CHUNKS], lx1[STAGE_CHUNKS];
+    // K-step g of the stream occupies W half 2g and X half 2g + 1; half h
+    // lives in buffer h % 5.
+    __shared__ uint4 ring[NBUF * BUF_CHUNKS];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -104,9 +127,7 @@ void fused_qkv_kernel(FusedArgs a) {
     // ---- tile schedule ---------------------------------------------------------
     // XCD x (workgroups b with b % 8 == x) owns a contiguous eighth of the
     // logical tile order; its G/8 workgroups walk that range G/8 tiles at a
-    // time, so the 8 XCDs sweep the W panels at the same pace (sharing them
-    // through the last-level cache) while each XCD's concurrent tiles share
-    // panels in its L2.
+    // time.
     const int G = gridDim.x;
     const int bid = blockIdx.x;
     const int total = a.tiles_m * a.tiles_n;
@@ -132,8 +153,11 @@ void fused_qkv_kernel(FusedArgs a) {
     };
 
     // ---- global -> LDS: direct loads (buffer_load ... lds) ----------------------
-    // Instruction i of wave w fills block b = 4 i + w of a stage: lane L brings
-    // chunk L % 8 of tile row 8 b + L / 8 to LDS offset 16 L of the block.
+    // Instruction i of wave w fills block b = 4 i + w of a half: lane L brings
+    // the chunk stored at position L % 8 of row L / 8 of the block, i.e. chunk
+    // (L % 8) ^ (b % 8) of panel row 8 b + L / 8; the eight lanes of a row fetch
+    // its whole 128-byte segment.  b % 8 = 4 (i % 2) + w, so even and odd
+    // instructions use two lane offsets that differ in bit 6.
     const __amdgpu_buffer_rsrc_t rw = __builtin_amdgcn_make_buffer_rsrc(
         (void*)a.w, (short)0, int(uint32_t(a.N) * uint32_t(K) * 2u), 0x00020000);
     const __amdgpu_buffer_rsrc_t rx = __builtin_amdgcn_make_buffer_rsrc(
@@ -142,79 +166,53 @@ void fused_qkv_kernel(FusedArgs a) {
     const uint32_t rowbytes = uint32_t(K) * 2u;
     const int wv = wave;
     const uint32_t lrow = uint32_t(8 * wv + (lane >> 3));
-    // this lane's byte offset of K-tile 0 of a tile's W panel (origin n0) or X
-    // panel (origin m0)
+    const uint32_t lchunk = uint32_t((lane & 7) ^ wv) * 16u;
+    // this lane's byte offset of K-step 0 of a panel at row origin (even
+    // instructions; odd ones: ^ 64)
     auto panel_offset = [&](int origin) {
-        return (uint32_t(origin) + lrow) * rowbytes + uint32_t(lane & 7) * 16u;
+        return (uint32_t(origin) + lrow) * rowbytes + lchunk;
     };
 
     // ---- fragment reads: lane i%32 owns MFMA row i%32 of each 32-row block ----
+    // Sub-step ks reads chunk 2 ks + hf of each row: the position of chunk hf
+    // with bits 1-2 flipped by 2 ks.  Byte offsets within a buffer:
     const int fr = lane & 31;
     const int hf = lane >> 5;
-    int woff[4], xoff[4];                                   // chunk index of row, chunk hf
+    uint32_t wo[4][4], xo[4][4];                           // [ks][block]
 #pragma unroll
-    for (int b = 0; b < 4; ++b) {
-        woff[b] = lds_chunk(wn * 128 + mfma_row(b, fr), hf);
-        xoff[b] = lds_chunk(wm * 128 + mfma_row(b, fr), hf);
-    }
-
-    f32x16 acc[4][4];
-
-    // Request K-tile kt of the panels at (gw0, gx0) into stage s: 2 x LOADS
-    // block loads per wave.
-    auto load_stage = [&](uint32_t gw0, uint32_t gx0, int kt, int s) {
-        const uint32_t kb = uint32_t(kt) * BK * 2u;
-        typedef __attribute__((address_space(3))) uint4 lds_uint4;
-        lds_uint4* dw = (lds_uint4*)((s ? lw1 : lw0) + wv * BLOCK_CHUNKS);
-        lds_uint4* dx = (lds_uint4*)((s ? lx1 : lx0) + wv * BLOCK_CHUNKS);
-#pragma unroll
-        for (int i = 0; i < LOADS; ++i) {
-            const uint32_t roff = uint32_t(32 * i) * rowbytes + kb;
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                rw, (__attribute__((address_space(3))) void*)(dw + 4 * i * BLOCK_CHUNKS), 16,
-                gw0 + roff, 0, 0, 0);
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                rx, (__attribute__((address_space(3))) void*)(dx + 4 * i * BLOCK_CHUNKS), 16,
-                gx0 + roff, 0, 0, 0);
-        }
-    };
-
-    // Fragments of one 16-K sub-step: four 32-row blocks of W (A operand) and of
-    // X (B operand); sub-step ks reads chunks 2 ks + hf.  Two sets, A and B.
-    bf16x8 fa_a[4], fb_a[4], fa_b[4], fb_b[4];
-    auto read_frags = [&](int s, int ks, bf16x8* fa, bf16x8* fb) {
-        const uint4* w = s ? lw1 : lw0;
-        const uint4* x = s ? lx1 : lx0;
+    for (int ks = 0; ks < 4; ++ks)
 #pragma unroll
         for (int b = 0; b < 4; ++b) {
-            fa[b] = __builtin_bit_cast(bf16x8, w[woff[b] + 2 * ks]);
-            fb[b] = __builtin_bit_cast(bf16x8, x[xoff[b] + 2 * ks]);
+            wo[ks][b] = uint32_t(lds_pos(wn * 128 + mfma_row(b, fr), hf) ^ (2 * ks)) * 16u;
+            xo[ks][b] = uint32_t(lds_pos(wm * 128 + mfma_row(b, fr), hf) ^ (2 * ks)) * 16u;
         }
+    typedef __attribute__((address_space(3))) uint4 lds_uint4;
+    lds_uint4* ring3 = (lds_uint4*)ring;
+    const uint32_t ring0 = uint32_t(reinterpret_cast<uintptr_t>(ring3));
+
+    f32x16 acc[4][4];
+    // fragments of one sub-step: four 32-row blocks of W (A operand) and of X
+    // (B operand); two sets, A and B
+    bf16x8 fa_a[4], fb_a[4], fa_b[4], fb_b[4];
+
+    // One MFMA on accumulator (nb, mb); `init`: the tile's first product, with
+    // a zero accumulator input (no separate zeroing).
+    auto mfma1 = [&](int nb, int mb, const bf16x8& fa, const bf16x8& fb, bool init) {
+        if (init)
+            asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0"
+                         : "=a"(acc[nb][mb]) : "v"(fa), "v"(fb));
+        else
+            asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0"
+                         : "+a"(acc[nb][mb]) : "v"(fa), "v"(fb));
     };
-    auto mfmas = [&](const bf16x8* fa, const bf16x8* fb) {
-#pragma unroll
-        for (int nb = 0; nb < 4; ++nb)
-#pragma unroll
-            for (int mb = 0; mb < 4; ++mb)
-                acc[nb][mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[nb], fb[mb], acc[nb][mb],
-                                                                     0, 0, 0);
+    // A fragment read.  Its result may only be used after a wait_lgkm that
+    // covers it: the compiler does not track it, and every use below is an
+    // MFMA placed after such a wait.
+    auto lds_read = [&](bf16x8& dst, uint32_t addr) {
+        asm volatile("ds_read_b128 %0, %1" : "=v"(dst) : "v"(addr));
     };
 
-    // ---- main loop ------------------------------------------------------------
-    // The K-tiles of this workgroup's output tiles form one stream.  The code
-    // between two workgroup barriers (one scheduling region) handles K-tile kt
-    // in stage s = kt % 2:
-    //   the sub-step-3 MFMAs of K-tile kt-1 (its fragments are in set B);
-    //   the loads of K-tile kt+1 into the other stage (free since the barrier),
-    //   one instruction per two MFMAs over the first half of the region, so
-    //   that the address unit never fills up and stalls the wave's in-order
-    //   MFMA issue, while the last load still has half a region to arrive;
-    //   the fragment reads of K-tile kt's four sub-steps and the MFMAs of its
-    //   sub-steps 0..2, each sub-step's reads overlapping the previous MFMAs;
-    // then a wait for this wave's loads and LDS reads, and the barrier.
-    // sched_group_barrier pins the interleaving (0x008 MFMA, 0x020 VMEM read,
-    // 0x100 DS read).
-    const int KT = K / BK;                                  // = 2 * heads: even
+    const int KT = K / BK;
     // Panels of the current tile and of this workgroup's next tile; past its
     // last tile the "next" requests re-read the current tile (in bounds, unused).
     int m0, n0, m0_next, n0_next;
@@ -223,42 +221,74 @@ void fused_qkv_kernel(FusedArgs a) {
     tile_origin(next < end ? next : first, m0_next, n0_next);
     uint32_t gw_cur = panel_offset(n0), gx_cur = panel_offset(m0);
     uint32_t gw_nxt = panel_offset(n0_next), gx_nxt = panel_offset(m0_next);
-    // load K-tile index kidx of the stream (kidx >= KT: the next output tile)
-    auto load_k = [&](int kidx, int stage) {
+
+    // Load instruction i (0..7) of the W or X half of K-step kidx of the
+    // stream (kidx >= KT: the next output tile) into buffer buf.
+    auto load_one = [&](bool is_w, int i, int kidx, int buf) {
         const bool nx = kidx >= KT;
-        load_stage(nx ? gw_nxt : gw_cur, nx ? gx_nxt : gx_cur, nx ? kidx - KT : kidx, stage);
+        const uint32_t g0 = is_w ? (nx ? gw_nxt : gw_cur) : (nx ? gx_nxt : gx_cur);
+        const uint32_t kb = uint32_t(nx ? kidx - KT : kidx) * BK * 2u;
+        const uint32_t roff = uint32_t(32 * i) * rowbytes + kb;
+        const uint32_t flip = (i & 1) ? 64u : 0u;
+        lds_uint4* dst = ring3 + buf * BUF_CHUNKS + (4 * i + wv) * 64;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(is_w ? rw : rx,
+                                                 (__attribute__((address_space(3))) void*)dst, 16,
+                                                 g0 ^ flip, roff, 0, 0);
     };
 
-    // Region of K-tile kt (stage s); `steady` adds the previous K-tile's
-    // sub-step-3 MFMAs and the loads of K-tile kt + 1.
-    auto region = [&](int kt, int s, bool steady) {
-        if (steady) {
-            mfmas(fa_b, fb_b);
-            load_k(kt + 1, s ^ 1);
-        }
-        read_frags(s, 0, fa_a, fb_a);
-        read_frags(s, 1, fa_b, fb_b);
-        mfmas(fa_a, fb_a);
-        read_frags(s, 2, fa_a, fb_a);
-        mfmas(fa_b, fb_b);
-        read_frags(s, 3, fa_b, fb_b);
-        mfmas(fa_a, fb_a);
-        if (steady) {
+    // ---- main loop ------------------------------------------------------------
+    // K-step kt of the current tile, W half in buffer pw.  64 MFMA slots in
+    // four phases of 16 (phase 0: set B, the previous K-step's sub-step 3; 1:
+    // set A, sub-step 0; 2: set B, sub-step 1; 3: set A, sub-step 2).  After
+    // slot j < 8 of phase p comes fragment read j of sub-step p into the other
+    // set (that set's MFMAs all issued in the previous phase); after every
+    // third slot one of the 16 load instructions of the X half of K-step kt+1
+    // and the W half of K-step kt+2, into the two buffers K-step kt-1 used.
+    // The step ends waiting for all but the last eight loads (the W half of
+    // kt+2, which stays in flight) and for the reads, then the barrier.  A
+    // tile's first step has no phase 0: its sub-step-0 fragments are read
+    // up front and phase 1 starts the accumulators.
+    int pw = 0;
+    auto step = [&](int kt, bool first_of_tile) {
+        const int px = pw == 4 ? 0 : pw + 1;
+        const int bx1 = pw >= 2 ? pw - 2 : pw + 3;       // (pw + 3) % 5
+        const int bw2 = pw >= 1 ? pw - 1 : 4;            // (pw + 4) % 5
+        const uint32_t wb = ring0 + uint32_t(pw) * (BUF_CHUNKS * 16);
+        const uint32_t xb = ring0 + uint32_t(px) * (BUF_CHUNKS * 16);
+        const int i0 = first_of_tile ? 16 : 0;
+        if (first_of_tile) {
 #pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
-                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-                __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+            for (int b = 0; b < 4; ++b) lds_read(fa_a[b], wb + wo[0][b]);
+#pragma unroll
+            for (int b = 0; b < 4; ++b) lds_read(fb_a[b], xb + xo[0][b]);
+        }
+#pragma unroll
+        for (int i = 0; i < 64; ++i) {
+            if (i < i0) continue;
+            const int ph = i >> 4, j = i & 15;
+            const int nb = j >> 2, mb = j & 3;
+            // The first row (nb 0) of a phase needs read 4 + mb of the previous
+            // phase's eight, in order; the j reads issued in this phase so far
+            // come after them: at most 3 - mb + j = 3 may be outstanding.
+            if (ph > 0 && j < 4) wait_lgkm<3>();
+            if (ph & 1)
+                mfma1(nb, mb, fa_a[nb], fb_a[mb], first_of_tile && ph == 1);
+            else
+                mfma1(nb, mb, fa_b[nb], fb_b[mb], false);
+            if (((i - i0) % LSTEP) == 0 && ((i - i0) / LSTEP) < 2 * HLOADS) {
+                const int v = (i - i0) / LSTEP;
+                if (v < HLOADS) load_one(false, v, kt + 1, bx1);
+                else load_one(true, v - HLOADS, kt + 2, bw2);
             }
-        } else {
-            __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+            if (j < 8) {
+                bf16x8* fa = (ph & 1) ? fa_b : fa_a;
+                bf16x8* fb = (ph & 1) ? fb_b : fb_a;
+                if (j < 4) lds_read(fa[j], wb + wo[ph][j]);
+                else lds_read(fb[j - 4], xb + xo[ph][j - 4]);
+            }
         }
-#pragma unroll
-        for (int i = 0; i < (steady ? 16 : 24); ++i) {
-            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-            __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
-        }
-        asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+        asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(HLOADS) : "memory");
+        pw = pw >= 3 ? pw - 3 : pw + 2;                  // (pw + 2) % 5
     };
 
     // ---- epilogue: one head (128 columns) per wave ----------------------------
@@ -268,7 +298,9 @@ void fused_qkv_kernel(FusedArgs a) {
     //   wm * 128 + mfma_row(mb, fr).
     // Registers q, q+4, q+8, q+12 hold four consecutive dims; n-blocks 2h and
     // 2h+1 continue each other (16 bytes of bf16); n-block nb+2 holds e + 64.
-  auto epilogue = [&](int m0, int n0) {
+    // Each m-block is read twice (sum of squares, then the outputs, four dims
+    // per n-block at a time), which keeps the VGPRs in use small.
+    auto epilogue = [&](int m0, int n0) {
     const int ncol = n0 + wn * 128;
     if (ncol >= a.N) return;
     const int p = ncol / a.hidden;                 // 0 q, 1 k, 2 v
@@ -289,117 +321,101 @@ void fused_qkv_kernel(FusedArgs a) {
         const int bidx = m / a.s_local;
         const int s = m - bidx * a.s_local;
         const int row = a.row0 + s;                 // sequence row == position
-        // Accumulators are read out of AGPRs one m-block at a time; written as
-        // explicit reads so that the compiler does not copy all 256 of them into
-        // VGPRs at the loop exit (which would spill).
-        float v[4][16];
-#pragma unroll
-        for (int nb = 0; nb < 4; ++nb)
-#pragma unroll
-            for (int r = 0; r < 16; ++r)
-                asm volatile("v_accvgpr_read_b32 %0, %1" : "=v"(v[nb][r]) : "a"(acc[nb][mb][r]));
-
+        uint16_t* orow = dbase + int64_t(bidx) * a.stride_b + int64_t(row) * a.stride_s;
+        const float* csr = a.cs + int64_t(row) * 128;
+        float inv = 1.f;
         if (qk) {
             // RMSNorm over the head's 128 values: 64 here, 64 in lane ^ 32
             float ss = 0.f;
 #pragma unroll
             for (int nb = 0; nb < 4; ++nb)
 #pragma unroll
-                for (int r = 0; r < 16; ++r) ss += v[nb][r] * v[nb][r];
+                for (int r = 0; r < 16; ++r) {
+                    const float t = acc_read(acc[nb][mb][r]);
+                    ss += t * t;
+                }
             ss += __shfl_xor(ss, 32);
-            const float inv = rsqrtf(ss * (1.0f / 128.0f) + a.eps);
-            const float* csr = a.cs + int64_t(row) * 128;
-            if (a.rope_interleaved) {
-                // pairs (2i, 2i+1): registers q + 4 g hold dims E + g, E = e(nb, q), so
-                // (E, E+1) and (E+2, E+3) sit in registers (q, q+4) and (q+8, q+12)
-                // and rotate by the angles of columns E/2 and E/2 + 1
+            inv = rsqrtf(ss * (1.0f / 128.0f) + a.eps);
+        }
 #pragma unroll
-                for (int nb = 0; nb < 4; ++nb) {
-                    f32x4 wt[4];
-                    f32x2 cv[4], sv[4];
+        for (int q = 0; q < 4; ++q) {
+            // v[nb][g] = dim e(nb, q) + g, g = 0..3 (registers q + 4 g)
+            float v[4][4];
 #pragma unroll
-                    for (int q = 0; q < 4; ++q) {
+            for (int nb = 0; nb < 4; ++nb)
+#pragma unroll
+                for (int g = 0; g < 4; ++g) v[nb][g] = acc_read(acc[nb][mb][q + 4 * g]);
+            if (qk) {
+                if (a.rope_interleaved) {
+                    // pairs (2i, 2i+1) = dims (E, E+1) and (E+2, E+3) of each
+                    // n-block, E = e(nb, q), rotated by the angles of table
+                    // columns E/2 and E/2 + 1
+#pragma unroll
+                    for (int nb = 0; nb < 4; ++nb) {
                         const int e = 64 * (nb >> 1) + 32 * hf + 8 * q + 4 * (nb & 1);
-                        wt[q] = *reinterpret_cast<const f32x4*>(nw + e);
-                        cv[q] = *reinterpret_cast<const f32x2*>(csr + e / 2);
-                        sv[q] = *reinterpret_cast<const f32x2*>(csr + 64 + e / 2);
-                    }
-#pragma unroll
-                    for (int q = 0; q < 4; ++q)
+                        const f32x4 wt = *reinterpret_cast<const f32x4*>(nw + e);
+                        const f32x2 cv = *reinterpret_cast<const f32x2*>(csr + e / 2);
+                        const f32x2 sv = *reinterpret_cast<const f32x2*>(csr + 64 + e / 2);
 #pragma unroll
                         for (int gp = 0; gp < 2; ++gp) {
-                            const int r0 = q + 8 * gp, r1 = r0 + 4;
-                            const float z0 = v[nb][r0] * (inv * wt[q][2 * gp]);
-                            const float z1 = v[nb][r1] * (inv * wt[q][2 * gp + 1]);
-                            v[nb][r0] = z0 * cv[q][gp] - z1 * sv[q][gp];
-                            v[nb][r1] = z1 * cv[q][gp] + z0 * sv[q][gp];
+                            const float z0 = v[nb][2 * gp] * (inv * wt[2 * gp]);
+                            const float z1 = v[nb][2 * gp + 1] * (inv * wt[2 * gp + 1]);
+                            v[nb][2 * gp] = z0 * cv[gp] - z1 * sv[gp];
+                            v[nb][2 * gp + 1] = z1 * cv[gp] + z0 * sv[gp];
                         }
-                }
-            } else
-            // rotate-half: n-blocks lo = nb and hi = nb + 2 hold dims e and e + 64
+                    }
+                } else {
+                    // rotate-half: n-blocks lo and lo + 2 hold dims e and e + 64
 #pragma unroll
-            for (int lo = 0; lo < 2; ++lo) {
-                f32x4 wl[4], wh[4], cv[4], sv[4];
+                    for (int lo = 0; lo < 2; ++lo) {
+                        const int e = 32 * hf + 8 * q + 4 * lo;
+                        const f32x4 wl = *reinterpret_cast<const f32x4*>(nw + e);
+                        const f32x4 wh = *reinterpret_cast<const f32x4*>(nw + 64 + e);
+                        const f32x4 cv = *reinterpret_cast<const f32x4*>(csr + e);
+                        const f32x4 sv = *reinterpret_cast<const f32x4*>(csr + 64 + e);
 #pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    const int e = 32 * hf + 8 * q + 4 * lo;
-                    wl[q] = *reinterpret_cast<const f32x4*>(nw + e);
-                    wh[q] = *reinterpret_cast<const f32x4*>(nw + 64 + e);
-                    cv[q] = *reinterpret_cast<const f32x4*>(csr + e);
-                    sv[q] = *reinterpret_cast<const f32x4*>(csr + 64 + e);
-                }
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const float zl = v[lo][r] * (inv * wl[r & 3][r >> 2]);
-                    const float zh = v[lo + 2][r] * (inv * wh[r & 3][r >> 2]);
-                    const float c = cv[r & 3][r >> 2];
-                    const float sn = sv[r & 3][r >> 2];
-                    v[lo][r] = zl * c - zh * sn;
-                    v[lo + 2][r] = zh * c + zl * sn;
+                        for (int g = 0; g < 4; ++g) {
+                            const float zl = v[lo][g] * (inv * wl[g]);
+                            const float zh = v[lo + 2][g] * (inv * wh[g]);
+                            v[lo][g] = zl * cv[g] - zh * sv[g];
+                            v[lo + 2][g] = zh * cv[g] + zl * sv[g];
+                        }
+                    }
                 }
             }
-        }
-        uint16_t* orow = dbase + int64_t(bidx) * a.stride_b + int64_t(row) * a.stride_s;
 #pragma unroll
-        for (int hh = 0; hh < 2; ++hh)
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
+            for (int hh = 0; hh < 2; ++hh) {
                 const int e = 64 * hh + 32 * hf + 8 * q;
                 uint4 pk;
-                pk.x = uint32_t(bf16_bits(v[2 * hh][q])) | (uint32_t(bf16_bits(v[2 * hh][q + 4])) << 16);
-                pk.y = uint32_t(bf16_bits(v[2 * hh][q + 8])) | (uint32_t(bf16_bits(v[2 * hh][q + 12])) << 16);
-                pk.z = uint32_t(bf16_bits(v[2 * hh + 1][q])) | (uint32_t(bf16_bits(v[2 * hh + 1][q + 4])) << 16);
-                pk.w = uint32_t(bf16_bits(v[2 * hh + 1][q + 8])) | (uint32_t(bf16_bits(v[2 * hh + 1][q + 12])) << 16);
+                pk.x = uint32_t(bf16_bits(v[2 * hh][0])) | (uint32_t(bf16_bits(v[2 * hh][1])) << 16);
+                pk.y = uint32_t(bf16_bits(v[2 * hh][2])) | (uint32_t(bf16_bits(v[2 * hh][3])) << 16);
+                pk.z = uint32_t(bf16_bits(v[2 * hh + 1][0])) |
+                       (uint32_t(bf16_bits(v[2 * hh + 1][1])) << 16);
+                pk.w = uint32_t(bf16_bits(v[2 * hh + 1][2])) |
+                       (uint32_t(bf16_bits(v[2 * hh + 1][3])) << 16);
                 if (in_range) *reinterpret_cast<uint4*>(orow + e) = pk;
             }
+        }
         __builtin_amdgcn_sched_barrier(0);
     }
   };
 
-
-    // prologue: K-tiles 0 and 1 of the first tile
-    load_stage(gw_cur, gx_cur, 0, 0);
-    load_stage(gw_cur, gx_cur, 1, 1);
-    asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(2 * LOADS) : "memory");
+    // prologue: W and X halves of K-step 0 and the W half of K-step 1
+#pragma unroll
+    for (int i = 0; i < HLOADS; ++i) load_one(true, i, 0, 0);
+#pragma unroll
+    for (int i = 0; i < HLOADS; ++i) load_one(false, i, 0, 1);
+#pragma unroll
+    for (int i = 0; i < HLOADS; ++i) load_one(true, i, 1, 2);
+    asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(HLOADS) : "memory");
     for (;;) {
+        step(0, true);
+        for (int kt = 1; kt < KT; ++kt) step(kt, false);
+        // sub-step 3 of the last K-step (its fragments arrived before the barrier)
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+        for (int nb = 0; nb < 4; ++nb)
 #pragma unroll
-            for (int j = 0; j < 4; ++j)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
-        // K-tile 1 was requested before this tile began (it overlapped the
-        // previous epilogue); K-tile 2 on is requested one region ahead
-        region(0, 0, false);
-        region(1, 1, true);
-        for (int kt = 2; kt < KT; kt += 2) {
-            region(kt, 0, true);
-            region(kt + 1, 1, true);
-        }
-        // the next tile's K-tile 0 is in stage 0; request its K-tile 1 into the
-        // (free) stage 1 so that it loads during the epilogue
-        load_k(KT + 1, 1);
-        mfmas(fa_b, fb_b);                          // sub-step 3 of the last K-tile
+            for (int mb = 0; mb < 4; ++mb) mfma1(nb, mb, fa_b[nb], fb_b[mb], false);
         // the nops give the last MFMAs' results the wait states an accumulator
         // read needs
         asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
@@ -444,7 +460,8 @@ hipError_t launch_fused(const FusedArgs& a_in, hipStream_t stream) {
     a.tiles_n = (a.N + BN - 1) / BN;
     a.group_m = GROUP_M;
     const int tiles = a.tiles_m * a.tiles_n;
-    const int grid = tiles < device_cus() ? tiles : device_cus();
+    const int cus = device_cus();
+    const int grid = tiles < cus ? tiles : cus;
     hipLaunchKernelGGL(fused_qkv_kernel, dim3(grid), dim3(NT), 0, stream, a);
     return hipGetLastError();
 }
