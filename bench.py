@@ -171,6 +171,137 @@ def output_side(hx, torch, wl, band, sched, dev, reps: int = 10):
     return out
 
 
+def readiness(hx, torch, wl, x, w, wq, wk, cs, dev, reps: int = 5):
+    """Forward with readiness words on one stream and a wait per destination on
+    its own stream: when each destination's receive slot becomes readable,
+    relative to the start of the call, and the call's own duration, beside the
+    same call without publishing."""
+    M = wl.tokens
+    sess = hx.qkvx_create(wl.hidden, wl.heads, 128, wl.world, wl.layout, M, wl.num_slots)
+    producer = torch.cuda.Stream()
+    consumers = [torch.cuda.Stream() for _ in range(wl.world)]
+    ev = lambda: torch.cuda.Event(enable_timing=True)
+    plain = []
+    for it in range(reps + 1):
+        e0, e1 = ev(), ev()
+        with torch.cuda.stream(producer):
+            e0.record(producer)
+            sess.forward(x, w, wq, wk, cs, wl.rank, producer)
+            e1.record(producer)
+        torch.cuda.synchronize()
+        if it:
+            plain.append(e0.elapsed_time(e1) * 1e3)
+    sess.set_publish(True)
+    fwd, ready = [], [[] for _ in range(wl.world)]
+    for it in range(reps + 1):
+        e0, e1 = ev(), ev()
+        ed = [ev() for _ in range(wl.world)]
+        with torch.cuda.stream(producer):
+            e0.record(producer)
+            sess.forward(x, w, wq, wk, cs, wl.rank, producer)
+            e1.record(producer)
+        for d, c in enumerate(consumers):
+            c.wait_event(e0)            # the waits start with the call
+            sess.wait_ready(d, stream=c)
+            ed[d].record(c)
+        torch.cuda.synchronize()
+        if it:
+            fwd.append(e0.elapsed_time(e1) * 1e3)
+            for d in range(wl.world):
+                ready[d].append(e0.elapsed_time(ed[d]) * 1e3)
+    timeouts = sess.ready_state()[1]
+    sess.close()
+    return {"forward_us": float(np.mean(plain)), "publishing_forward_us": float(np.mean(fwd)),
+            "dest_ready_us": [float(np.mean(r)) for r in ready], "wait_timeouts": timeouts}
+
+
+def head_chunk_pipeline(hx, torch, wl, q, k, v, sched, dev, reps: int = 5):
+    """The pages' three-stream head-chunk schedule on one GPU: the input pack
+    of chunk N+1, a stand-in consumer of chunk N and the output side of chunk
+    N-1 overlap on three streams joined by events, against the same work on
+    one stream.  Per chunk: pack Q|K|V of the band into a receive slot
+    [B, S_global, hc, 384] (rows rank*S_local..); consumer: a bf16 matmul of
+    the slot's q part by a [hc*128, hc*128] weight (a stand-in for attention,
+    which is not part of this path) giving the output band [B, S_global, hc,
+    128]; output side: its sequence split into the peers' received bands and
+    the merge of the received band into the full output."""
+    S, U, hl, B = wl.s_local, wl.world, wl.local_heads, wl.batch
+    Sg = wl.s_global
+    slots = {c: [torch.empty(B, Sg, c, 384, dtype=torch.bfloat16, device=dev) for _ in range(U)]
+             for _, c in sched}
+    wts = {c: torch.randn(c * 128, c * 128, device=dev).to(torch.bfloat16) / (c * 128) ** 0.5
+           for _, c in sched}
+    obands = {c: torch.empty(B, Sg, c, 128, dtype=torch.bfloat16, device=dev) for _, c in sched}
+    received = {c: [torch.empty(B, S, U * c, 128, dtype=torch.bfloat16, device=dev)
+                    for _ in range(U)] for _, c in sched}
+    out = torch.empty(B, S, wl.heads, 128, dtype=torch.bfloat16, device=dev)
+
+    def stage_in(i, st):
+        c = sched[i][1]
+        hx.ulysses_pack_qkv_head_chunk(q, k, v, world=U, schedule=wl.schedule, chunk=i,
+                                       dst=slots[c], row_offset=wl.rank * S, stream=st)
+
+    def stage_att(i, st):
+        c = sched[i][1]
+        with torch.cuda.stream(st):
+            qp = slots[c][0][..., :128].reshape(B * Sg, c * 128)
+            torch.matmul(qp.contiguous(), wts[c], out=obands[c].view(B * Sg, c * 128))
+
+    def stage_out(i, st):
+        off, c = sched[i]
+        hx.ulysses_pack_output_sequence_chunk(obands[c], world=U, dst=received[c],
+                                              head_offset=wl.rank * c, stream=st)
+        hx.ulysses_merge_output_head_chunk([received[c][0][:, :, u * c:(u + 1) * c]
+                                            for u in range(U)], world=U, local_heads=hl,
+                                           schedule=wl.schedule, chunk=i, out=out, stream=st)
+
+    main = torch.cuda.current_stream()
+    s_in, s_att, s_out = torch.cuda.Stream(), torch.cuda.Stream(), torch.cuda.Stream()
+    ev = lambda: torch.cuda.Event(enable_timing=True)
+
+    def sequential():
+        for i in range(len(sched)):
+            stage_in(i, main)
+            stage_att(i, main)
+            stage_out(i, main)
+
+    def pipelined():
+        start = torch.cuda.Event()
+        start.record(main)
+        for st in (s_in, s_att, s_out):
+            st.wait_event(start)
+        e_in = [torch.cuda.Event() for _ in sched]
+        e_att = [torch.cuda.Event() for _ in sched]
+        e_out = [torch.cuda.Event() for _ in sched]
+        for i in range(len(sched)):
+            stage_in(i, s_in)
+            e_in[i].record(s_in)
+            s_att.wait_event(e_in[i])
+            stage_att(i, s_att)
+            e_att[i].record(s_att)
+            s_out.wait_event(e_att[i])
+            stage_out(i, s_out)
+            e_out[i].record(s_out)
+        main.wait_event(e_out[-1])
+        for st in (s_in, s_att):
+            main.wait_stream(st)
+
+    res = {}
+    for name, fn in (("sequential_us", sequential), ("pipelined_us", pipelined)):
+        fn()
+        torch.cuda.synchronize()
+        e0, e1 = ev(), ev()
+        e0.record(main)
+        for _ in range(reps):
+            fn()
+        e1.record(main)
+        torch.cuda.synchronize()
+        res[name] = e0.elapsed_time(e1) * 1e3 / reps
+    res["speedup"] = res["sequential_us"] / res["pipelined_us"]
+    res["consumer"] = "bf16 matmul of the q band by a [hc*128, hc*128] weight (stand-in)"
+    return res
+
+
 def main():
     args = parse()
     world_env = int(os.environ.get("WORLD_SIZE", "1"))
@@ -298,6 +429,8 @@ def main():
         "kernels_ms": {"fused": fused_ms, "pack_all_chunks": pack_ms, "merge_all_chunks": merge_ms},
     }
     result["output_side"] = output_side(hx, torch, wl, band, sched, dev)
+    result["readiness"] = readiness(hx, torch, wl, x, w, wq, wk, cs, dev)
+    result["head_chunk_pipeline"] = head_chunk_pipeline(hx, torch, wl, q, k, v, sched, dev)
     if calib:
         result["copy_calibration"] = calib
     if not args.skip_cpu_baseline:

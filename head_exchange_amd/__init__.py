@@ -28,7 +28,8 @@ EXPORTS = ("qkvx_last_error", "qkvx_slot_bytes", "qkvx_create", "qkvx_forward",
            "qkvx_last_outputs", "qkvx_poison_receive_slots", "qkvx_describe",
            "qkvx_destroy", "ulysses_pack_qkv_head_chunk", "ulysses_merge_output_head_chunk",
            "ulysses_scatter_heads", "ulysses_gather_heads", "ulysses_pack_output_sequence_chunk",
-           "ulysses_exchange_chunks")
+           "ulysses_exchange_chunks", "qkvx_set_publish", "qkvx_wait_ready", "qkvx_wait_word",
+           "qkvx_ready_state", "qkvx_ready_expected")
 
 
 class QkvxError(RuntimeError):
@@ -96,6 +97,17 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.qkvx_describe.argtypes = [vp, ctypes.c_char_p, sz]
     lib.qkvx_destroy.restype = i32
     lib.qkvx_destroy.argtypes = [vp]
+    u64p = ctypes.POINTER(ctypes.c_ulonglong)
+    lib.qkvx_set_publish.restype = i32
+    lib.qkvx_set_publish.argtypes = [vp, i32]
+    lib.qkvx_wait_ready.restype = i32
+    lib.qkvx_wait_ready.argtypes = [vp, i32, i32, vp]
+    lib.qkvx_wait_word.restype = i32
+    lib.qkvx_wait_word.argtypes = [vp, ctypes.c_ulonglong, i32, vp, vp]
+    lib.qkvx_ready_state.restype = i32
+    lib.qkvx_ready_state.argtypes = [vp, u64p, ctypes.POINTER(ctypes.c_int)]
+    lib.qkvx_ready_expected.restype = i32
+    lib.qkvx_ready_expected.argtypes = [vp, u64p]
     lib.ulysses_pack_qkv_head_chunk.restype = i32
     lib.ulysses_pack_qkv_head_chunk.argtypes = [
         ctypes.POINTER(View4), ctypes.POINTER(View4), ctypes.POINTER(View4), i32,
@@ -256,6 +268,27 @@ class Session:
     def last_outputs(self):
         return self._views(self.outputs_struct())
 
+    # ---- readiness words ----------------------------------------------------
+    def set_publish(self, enable: bool = True) -> None:
+        """Later forward calls publish per-destination readiness words."""
+        _check(load().qkvx_set_publish(self._h, int(bool(enable))))
+
+    def wait_ready(self, dest: int, spin_limit: int = 1 << 22, stream=None) -> None:
+        """Enqueue on ``stream`` a wait for destination ``dest`` of the last call."""
+        _check(load().qkvx_wait_ready(self._h, dest, spin_limit, _stream(stream)))
+
+    def ready_state(self):
+        """(current readiness words, timeout count), read synchronously."""
+        words = (ctypes.c_ulonglong * self.world)()
+        t = ctypes.c_int(0)
+        _check(load().qkvx_ready_state(self._h, words, ctypes.byref(t)))
+        return list(words), t.value
+
+    def ready_expected(self):
+        words = (ctypes.c_ulonglong * self.world)()
+        _check(load().qkvx_ready_expected(self._h, words))
+        return list(words)
+
     def poison_receive_slots(self, stream=None) -> None:
         _check(load().qkvx_poison_receive_slots(self._h, _stream(stream)))
 
@@ -376,3 +409,11 @@ def ulysses_exchange_chunks(x, *, world: int, rank: int, dst: Sequence, stream=N
     ptrs = (ctypes.c_void_p * world)(*[t.data_ptr() for t in dst])
     _check(load().ulysses_exchange_chunks(x.data_ptr(), world, chunk_bytes, rank, ptrs,
                                           _stream(stream)))
+
+
+def qkvx_wait_word(word, expected: int, timeouts, *, spin_limit: int = 1 << 22,
+                   stream=None) -> None:
+    """Enqueue the wait kernel on a device uint64 ``word`` (a one-element int64
+    tensor); a timeout adds 1 to the device int32 ``timeouts`` tensor."""
+    _check(load().qkvx_wait_word(word.data_ptr(), int(expected), spin_limit, timeouts.data_ptr(),
+                                 _stream(stream)))

@@ -17,7 +17,7 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libqkvx.so")
 OBJDIR = os.path.join(ROOT, "_build")
-SOURCES = ["qkvx_host.cpp", "qkvx_fused.hip", "qkvx_transport.hip"]
+SOURCES = ["qkvx_host.cpp", "qkvx_fused.hip", "qkvx_transport.hip", "qkvx_ready.hip"]
 
 ARCH = "gfx950"
 FLAGS = [

@@ -127,12 +127,13 @@ void fused_qkv_kernel(FusedArgs a) {
     // ---- tile schedule ---------------------------------------------------------
     // XCD x (workgroups b with b % 8 == x) owns a contiguous eighth of the
     // logical tile order; its G/8 workgroups walk that range G/8 tiles at a
-    // time.
+    // time.  With readiness words the whole grid walks the order together
+    // instead (tile b + G i), so that destinations complete one after another.
     const int G = gridDim.x;
     const int bid = blockIdx.x;
     const int total = a.tiles_m * a.tiles_n;
     int first, stride, end;
-    if (G % NXCD == 0) {
+    if (G % NXCD == 0 && !a.ready) {
         const int x = bid % NXCD;
         const int per = total / NXCD, rem = total % NXCD;
         first = x * per + min(x, rem) + bid / NXCD;
@@ -145,9 +146,21 @@ void fused_qkv_kernel(FusedArgs a) {
     }
     if (first >= end) return;
     const int K = a.K;
+    // With readiness words the order is destination-major: the tiles holding
+    // destination d's heads (dest_cols columns in each of q, k, v) come before
+    // those of d + 1, so early destinations are complete early.
     auto tile_origin = [&](int l, int& m0, int& n0) {
         int tm, tn;
-        tile_coords(l, a.tiles_m, a.tiles_n, a.group_m, tm, tn);
+        if (a.ready && a.dest_cols > 0) {
+            const int per_dest = a.tiles_m * 3 * a.dest_cols;
+            const int d = l / per_dest;
+            int c;
+            tile_coords(l - d * per_dest, a.tiles_m, 3 * a.dest_cols, a.group_m, tm, c);
+            const int p = c / a.dest_cols;
+            tn = p * a.part_cols + d * a.dest_cols + (c - p * a.dest_cols);
+        } else {
+            tile_coords(l, a.tiles_m, a.tiles_n, a.group_m, tm, tn);
+        }
         m0 = tm * BM;
         n0 = tn * BN;
     };
@@ -420,6 +433,24 @@ void fused_qkv_kernel(FusedArgs a) {
         // read needs
         asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
         epilogue(m0, n0);
+        if (a.ready) {
+            // publish: once all four waves' stores of this tile are complete,
+            // release them at agent scope and count the tile's two heads (two
+            // waves each) for their destinations
+            asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+            if (wave == 0) {
+                __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+                if (lane < 2) {
+                    const int ncol = n0 + lane * 128;
+                    if (ncol < a.N) {
+                        const int p = ncol / a.hidden;
+                        const int h = (ncol - p * a.hidden) >> 7;
+                        __hip_atomic_fetch_add(a.ready + h / a.local_heads, 2ull,
+                                               __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    }
+                }
+            }
+        }
         if (next >= end) break;
         m0 = m0_next;
         n0 = n0_next;
@@ -460,7 +491,9 @@ hipError_t launch_fused(const FusedArgs& a_in, hipStream_t stream) {
     a.tiles_n = (a.N + BN - 1) / BN;
     a.group_m = GROUP_M;
     const int tiles = a.tiles_m * a.tiles_n;
-    const int cus = device_cus();
+    // with readiness words one CU per XCD stays free, so that wait kernels on
+    // other streams always find room while this grid runs
+    const int cus = a.ready ? device_cus() - NXCD : device_cus();
     const int grid = tiles < cus ? tiles : cus;
     hipLaunchKernelGGL(fused_qkv_kernel, dim3(grid), dim3(NT), 0, stream, a);
     return hipGetLastError();

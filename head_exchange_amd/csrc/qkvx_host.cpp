@@ -143,6 +143,11 @@ struct qkvx_session {
     uint16_t* slots;            // num_slots * world regions
     size_t slot_bytes;
     bool owns_slots;
+    bool publish;                      // forward calls publish readiness words
+    bool last_published;               // the last call did
+    unsigned long long* ready;         // device: QKVX_MAX_WORLD readiness words
+    int* timeouts;                     // device: wait-kernel timeout counter
+    unsigned long long expect[QKVX_MAX_WORLD];   // word values after the last publishing call
     int64_t calls;              // successful forward calls so far
     bool has_last;
     qkvx_outputs last;
@@ -222,12 +227,18 @@ int qkvx_create(int hidden, int num_heads, int head_dim, int world, int layout, 
     s->owns_slots = owns;
     s->calls = 0;
     s->has_last = false;
+    s->publish = false;
+    s->last_published = false;
+    s->ready = nullptr;
+    s->timeouts = nullptr;
+    memset(s->expect, 0, sizeof(s->expect));
     *out = s;
     return ok();
 }
 
 int qkvx_destroy(qkvx_session* s) {
     if (!s) return fail(QKVX_ERR_INVALID, "session is NULL");
+    if (s->ready) hipFree(s->ready);
     if (s->owns_slots) {
         hipError_t e = hipFree(s->slots);
         delete s;
@@ -325,9 +336,20 @@ int qkvx_forward(qkvx_session* s, const void* x, int batch, int s_local, const v
     a.row0 = rank * s_local;
     a.rope_interleaved = s->rope == QKVX_ROPE_INTERLEAVED;
     a.eps = 1e-6f;
+    if (s->publish) {
+        a.ready = s->ready;
+        const int hl = s->heads / s->world;
+        a.dest_cols = (hl % 2 == 0 && hidden % 256 == 0) ? hl / 2 : 0;
+        a.part_cols = int32_t(hidden / 256);
+    }
     hipError_t e = launch_fused(a, static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return hip_fail(e, "fused projection launch");
     s->calls += 1;
+    s->last_published = s->publish;
+    if (s->publish) {
+        const unsigned long long inc = ready_increment(M, s->heads / s->world);
+        for (int d = 0; d < s->world; ++d) s->expect[d] += inc;
+    }
     s->last = o;
     s->has_last = true;
     if (out) *out = o;
@@ -358,14 +380,15 @@ int qkvx_describe(const qkvx_session* s, char* buf, size_t len) {
         "{\"hidden\": %d, \"num_heads\": %d, \"head_dim\": %d, \"world\": %d, "
         "\"local_heads\": %d, \"layout\": \"%s\", \"max_tokens\": %lld, \"num_slots\": %d, "
         "\"region_elems\": %lld, \"slot_bytes\": %zu, \"owns_slots\": %s, \"calls\": %lld, "
-        "\"next_slot\": %d, \"rope\": \"%s\", \"eps\": 1e-6, "
+        "\"next_slot\": %d, \"rope\": \"%s\", \"publish\": %s, \"eps\": 1e-6, "
         "\"tile\": {\"block_m\": %d, \"block_n\": %d, \"block_k\": %d, \"threads\": %d, "
         "\"group_m\": %d, \"mfma\": \"v_mfma_f32_32x32x16_bf16\", \"xcd_remap\": 8}}",
         s->hidden, s->heads, QKVX_HEAD_DIM, s->world, s->heads / s->world,
         s->layout == QKVX_LAYOUT_BSHD ? "bshd" : "fused", (long long)s->max_tokens,
         s->num_slots, (long long)s->region_elems, s->slot_bytes, s->owns_slots ? "true" : "false",
         (long long)s->calls, int(s->calls % s->num_slots),
-        s->rope == QKVX_ROPE_INTERLEAVED ? "interleaved" : "rotate_half", p.block_m, p.block_n, p.block_k,
+        s->rope == QKVX_ROPE_INTERLEAVED ? "interleaved" : "rotate_half",
+        s->publish ? "true" : "false", p.block_m, p.block_n, p.block_k,
         p.threads, p.group_m);
     if (buf && len) {
         size_t c = size_t(n) < len ? size_t(n) : len - 1;
@@ -379,6 +402,70 @@ int qkvx_describe(const qkvx_session* s, char* buf, size_t len) {
 // ===========================================================================
 // head-chunk transport
 // ===========================================================================
+
+// ===========================================================================
+// readiness words
+// ===========================================================================
+
+int qkvx_set_publish(qkvx_session* s, int enable) {
+    if (!s) return fail(QKVX_ERR_INVALID, "session is NULL");
+    if (enable && !s->ready) {
+        // words and the timeout counter in one allocation, zeroed once
+        void* mem = nullptr;
+        const size_t bytes = sizeof(unsigned long long) * QKVX_MAX_WORLD + 256;
+        hipError_t e = hipMalloc(&mem, bytes);
+        if (e == hipSuccess) e = hipMemset(mem, 0, bytes);
+        if (e != hipSuccess) {
+            if (mem) hipFree(mem);
+            return hip_fail(e, "allocation of the readiness words");
+        }
+        s->ready = static_cast<unsigned long long*>(mem);
+        s->timeouts = reinterpret_cast<int*>(static_cast<char*>(mem) +
+                                             sizeof(unsigned long long) * QKVX_MAX_WORLD);
+    }
+    s->publish = enable != 0;
+    return ok();
+}
+
+int qkvx_wait_word(const unsigned long long* word, unsigned long long expected, int spin_limit,
+                   int* timeouts, void* stream) {
+    if (!word || !timeouts) return fail(QKVX_ERR_INVALID, "word and timeouts must be non-NULL");
+    if ((reinterpret_cast<uintptr_t>(word) & 7u) || (reinterpret_cast<uintptr_t>(timeouts) & 3u))
+        return fail(QKVX_ERR_ALIGNMENT, "word must be 8-byte and timeouts 4-byte aligned");
+    if (spin_limit < 0) return fail(QKVX_ERR_INVALID, "spin_limit must be >= 0");
+    hipError_t e = launch_wait_word(word, expected, spin_limit, timeouts,
+                                    static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "wait kernel launch");
+    return ok();
+}
+
+int qkvx_wait_ready(qkvx_session* s, int dest, int spin_limit, void* stream) {
+    if (!s) return fail(QKVX_ERR_INVALID, "session is NULL");
+    if (!s->has_last || !s->last_published)
+        return fail(QKVX_ERR_INVALID, "the session's last call did not publish readiness words");
+    if (dest < 0 || dest >= s->world)
+        return fail(QKVX_ERR_INVALID, "dest %d outside [0, %d)", dest, s->world);
+    return qkvx_wait_word(s->ready + dest, s->expect[dest], spin_limit, s->timeouts, stream);
+}
+
+int qkvx_ready_state(qkvx_session* s, unsigned long long* words, int* timeouts) {
+    if (!s) return fail(QKVX_ERR_INVALID, "session is NULL");
+    if (!s->ready) return fail(QKVX_ERR_INVALID, "readiness words were never enabled");
+    hipError_t e = hipSuccess;
+    if (words)
+        e = hipMemcpy(words, s->ready, sizeof(unsigned long long) * s->world,
+                      hipMemcpyDeviceToHost);
+    if (e == hipSuccess && timeouts)
+        e = hipMemcpy(timeouts, s->timeouts, sizeof(int), hipMemcpyDeviceToHost);
+    if (e != hipSuccess) return hip_fail(e, "reading the readiness words");
+    return ok();
+}
+
+int qkvx_ready_expected(const qkvx_session* s, unsigned long long* words) {
+    if (!s || !words) return fail(QKVX_ERR_INVALID, "session and words must be non-NULL");
+    for (int d = 0; d < s->world; ++d) words[d] = s->expect[d];
+    return ok();
+}
 
 static int check_view(const qkvx_view4* v, const char* name) {
     if (!v) return fail(QKVX_ERR_INVALID, "%s is NULL", name);

@@ -64,7 +64,18 @@ struct FusedArgs {
     int32_t group_m;          // tile-row group of the tile order
     int32_t rope_interleaved; // 0: pairs (i, i + 64); 1: pairs (2i, 2i + 1)
     float eps;
+    // Readiness words (null: not published).  ready[d] grows by 2 for every
+    // (m-tile, head of destination d) stored, after the stores are released
+    // at agent scope; tiles then run destination by destination.
+    unsigned long long* ready;
+    int32_t dest_cols;        // 256-column tiles per destination and part (H_local / 2)
+    int32_t part_cols;        // 256-column tiles per part (hidden / 256)
 };
+
+// Readiness: a call adds this much to ready[d] of every destination d.
+inline unsigned long long ready_increment(int64_t M, int local_heads) {
+    return (unsigned long long)((M + 255) / 256) * 6ull * (unsigned long long)local_heads;
+}
 
 // ---------------------------------------------------------------------------
 // pack / merge kernel arguments
@@ -108,6 +119,10 @@ hipError_t launch_band_copy(const BandCopyArgs& a, int world, hipStream_t stream
 // vec16: chunk and every address are multiples of 16 bytes
 hipError_t launch_chunks(const ChunkArgs& a, int world, bool vec16, hipStream_t stream);
 hipError_t launch_fill16(uint16_t* p, int64_t n, uint16_t value, hipStream_t stream);
+// One-wave kernel: waits until *word >= expected (agent-scope acquire), polling
+// at most spin_limit times; on a timeout it adds 1 to *timeouts and returns.
+hipError_t launch_wait_word(const unsigned long long* word, unsigned long long expected,
+                            int spin_limit, int* timeouts, hipStream_t stream);
 
 // Tile plan of the fused kernel (exposed for describe()).
 struct FusedPlan {

@@ -317,6 +317,23 @@ def test_exchange_rejects_null_array(lib):
     assert lib.ulysses_exchange_chunks(ctypes.c_void_p(SRC[0]), 2, 16, 0, None, None) == -1
 
 
+def test_readiness_calls_reject(lib):
+    st, h = create(lib)
+    assert st == 0
+    assert lib.qkvx_wait_ready(h, 0, 10, None) == -1          # no publishing call yet
+    assert lib.qkvx_set_publish(h, 0) == 0                     # disabling allocates nothing
+    assert lib.qkvx_ready_state(h, None, None) == -1           # words never enabled
+    words = (ctypes.c_ulonglong * 2)(7, 7)
+    assert lib.qkvx_ready_expected(h, words) == 0 and list(words) == [0, 0]
+    assert lib.qkvx_set_publish(None, 1) == -1
+    assert lib.qkvx_destroy(h) == 0
+    assert lib.qkvx_wait_word(None, 1, 10, ctypes.c_void_p(FAKE), None) == -1
+    assert lib.qkvx_wait_word(ctypes.c_void_p(FAKE), 1, 10, None, None) == -1
+    assert lib.qkvx_wait_word(ctypes.c_void_p(FAKE + 4), 1, 10, ctypes.c_void_p(FAKE), None) == -4
+    assert lib.qkvx_wait_word(ctypes.c_void_p(FAKE), 1, 10, ctypes.c_void_p(FAKE + 2), None) == -4
+    assert lib.qkvx_wait_word(ctypes.c_void_p(FAKE), 1, -1, ctypes.c_void_p(FAKE), None) == -1
+
+
 def test_python_binding_fails_loudly_without_library(tmp_path):
     import importlib
     mod = importlib.reload(hx)
