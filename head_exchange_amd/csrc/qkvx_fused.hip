@@ -33,7 +33,8 @@
 //  * The main loop is a fixed sequence per K-step: 64 MFMA slots in four
 //    phases (each phase one 16-deep sub-step of all 16 accumulators), the next
 //    sub-step's eight fragment reads right after the first eight MFMAs of a
-//    phase, and the 16 load instructions one per three MFMAs.  MFMAs and
+//    phase, and the 16 load instructions in the other half of the slots (a
+//    load holds the wave's issue for ~24 cycles).  MFMAs and
 //    fragment reads are written as inline assembly with explicit
 //    lgkmcnt waits: the buffer a read uses is only known at run time, and
 //    the compiler, unable to tell it from the buffers being loaded, would
@@ -59,7 +60,6 @@ constexpr int NXCD = 8;
 constexpr int NBUF = 5;        // ring of half-step buffers
 constexpr int BUF_CHUNKS = 2048;    // 16-byte chunks per buffer: 256 rows x 128 bytes
 constexpr int HLOADS = 8;      // load instructions per wave per half step
-constexpr int LSTEP = 3;       // MFMA slots per load instruction
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
@@ -254,9 +254,10 @@ void fused_qkv_kernel(FusedArgs a) {
     // four phases of 16 (phase 0: set B, the previous K-step's sub-step 3; 1:
     // set A, sub-step 0; 2: set B, sub-step 1; 3: set A, sub-step 2).  After
     // slot j < 8 of phase p comes fragment read j of sub-step p into the other
-    // set (that set's MFMAs all issued in the previous phase); after every
-    // third slot one of the 16 load instructions of the X half of K-step kt+1
-    // and the W half of K-step kt+2, into the two buffers K-step kt-1 used.
+    // set (that set's MFMAs all issued in the previous phase); after slots
+    // j = 8, 10, 12, 14 one of the 16 load instructions of the X half of
+    // K-step kt+1 and the W half of K-step kt+2, into the two buffers K-step
+    // kt-1 used.
     // The step ends waiting for all but the last eight loads (the W half of
     // kt+2, which stays in flight) and for the reads, then the barrier.  A
     // tile's first step has no phase 0: its sub-step-0 fragments are read
@@ -288,8 +289,13 @@ void fused_qkv_kernel(FusedArgs a) {
                 mfma1(nb, mb, fa_a[nb], fb_a[mb], first_of_tile && ph == 1);
             else
                 mfma1(nb, mb, fa_b[nb], fb_b[mb], false);
-            if (((i - i0) % LSTEP) == 0 && ((i - i0) / LSTEP) < 2 * HLOADS) {
-                const int v = (i - i0) / LSTEP;
+            // Loads go only into slots without a fragment read (j >= 8): a
+            // load instruction holds the wave's issue for ~24 cycles while it
+            // sends 64 addresses, which must fit beside the slot's MFMA.
+            // Steady steps use j = 8, 10, 12, 14 of every phase; a tile's
+            // first step every slot j >= 8 of phases 1 and 2.
+            const int v = first_of_tile ? ((ph - 1) * 8 + (j - 8)) : (ph * 4 + (j - 8) / 2);
+            if (j >= 8 && (first_of_tile ? ph <= 2 : (j & 1) == 0) && v < 2 * HLOADS) {
                 if (v < HLOADS) load_one(false, v, kt + 1, bx1);
                 else load_one(true, v - HLOADS, kt + 2, bw2);
             }
