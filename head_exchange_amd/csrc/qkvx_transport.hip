@@ -15,7 +15,8 @@
 // The peer index (d or u) is blockIdx.y, so the peer's base pointers are
 // wave-uniform kernel arguments and no per-lane table lookup is needed; the rest
 // of the flat 16-byte-chunk index is split with precomputed 32-bit dividers.
-// Each thread moves one 16-byte vector with nontemporal accesses.
+// Each thread moves one 16-byte vector with nontemporal accesses (four for
+// small band copies).
 #include "qkvx_internal.h"
 
 namespace qkvx {
@@ -55,17 +56,31 @@ __global__ __launch_bounds__(kThreads) void pack_kernel(PackArgs a) {
     store_nt(dst, load_nt(src));
 }
 
+// VPT vectors per thread, kThreads * gridDim.x apart: small copies run with
+// VPT = 4 (a quarter of the workgroups to dispatch, four loads in flight per
+// thread), large ones with VPT = 1, which streams best.
+template <int VPT>
 __global__ __launch_bounds__(kThreads) void band_copy_kernel(BandCopyArgs a) {
     const uint32_t y = blockIdx.y;
-    const uint32_t c = blockIdx.x * kThreads + threadIdx.x;
-    if (c >= a.total) return;
-    const uint32_t e16 = c & 15u;
-    uint32_t tok, j, b, s;
-    a.div_hc.divmod(c >> 4, tok, j);
-    a.div_s.divmod(tok, b, s);
-    const uint16_t* src = a.src[y] + b * a.sb + s * a.ss + j * a.sh + e16 * 8;
-    uint16_t* dst = a.dst[y] + b * a.db + s * a.ds + j * a.dh + e16 * 8;
-    store_nt(dst, load_nt(src));
+    const uint32_t step = gridDim.x * kThreads;
+    const uint32_t c0 = blockIdx.x * kThreads + threadIdx.x;
+    u32x4 v[VPT];
+    uint16_t* dst[VPT];
+#pragma unroll
+    for (int k = 0; k < VPT; ++k) {
+        const uint32_t c = c0 + k * step;
+        dst[k] = nullptr;
+        if (c >= a.total) continue;
+        const uint32_t e16 = c & 15u;
+        uint32_t tok, j, b, s;
+        a.div_hc.divmod(c >> 4, tok, j);
+        a.div_s.divmod(tok, b, s);
+        dst[k] = a.dst[y] + b * a.db + s * a.ds + j * a.dh + e16 * 8;
+        v[k] = load_nt(a.src[y] + b * a.sb + s * a.ss + j * a.sh + e16 * 8);
+    }
+#pragma unroll
+    for (int k = 0; k < VPT; ++k)
+        if (dst[k]) store_nt(dst[k], v[k]);
 }
 
 // Byte chunks, 16 bytes per thread (chunk and addresses 16-byte aligned).
@@ -109,8 +124,13 @@ hipError_t launch_pack(const PackArgs& a, int world, hipStream_t stream) {
 
 hipError_t launch_band_copy(const BandCopyArgs& a, int world, hipStream_t stream) {
     if (a.total == 0) return hipSuccess;
-    dim3 grid((a.total + kThreads - 1) / kThreads, world);
-    hipLaunchKernelGGL(band_copy_kernel, grid, dim3(kThreads), 0, stream, a);
+    if (a.total < (1u << 20)) {                       // under 16 MB per peer
+        dim3 grid((a.total + 4 * kThreads - 1) / (4 * kThreads), world);
+        hipLaunchKernelGGL(band_copy_kernel<4>, grid, dim3(kThreads), 0, stream, a);
+    } else {
+        dim3 grid((a.total + kThreads - 1) / kThreads, world);
+        hipLaunchKernelGGL(band_copy_kernel<1>, grid, dim3(kThreads), 0, stream, a);
+    }
     return hipGetLastError();
 }
 
