@@ -241,12 +241,16 @@ void fused_qkv_kernel(FusedArgs a) {
         const bool nx = kidx >= KT;
         const uint32_t g0 = is_w ? (nx ? gw_nxt : gw_cur) : (nx ? gx_nxt : gx_cur);
         const uint32_t kb = uint32_t(nx ? kidx - KT : kidx) * BK * 2u;
-        const uint32_t roff = uint32_t(32 * i) * rowbytes + kb;
         const uint32_t flip = (i & 1) ? 64u : 0u;
         lds_uint4* dst = ring3 + buf * BUF_CHUNKS + (4 * i + wv) * 64;
+        // The row goes into the VGPR offset, which the buffer's range check
+        // covers (rows past M or N read as zero); only the K offset within a
+        // row, which keeps an in-range row in range, goes into the SGPR
+        // offset, which the check leaves out.
         __builtin_amdgcn_raw_ptr_buffer_load_lds(is_w ? rw : rx,
                                                  (__attribute__((address_space(3))) void*)dst, 16,
-                                                 g0 ^ flip, roff, 0, 0);
+                                                 (g0 ^ flip) + uint32_t(32 * i) * rowbytes, kb,
+                                                 0, 0);
     };
 
     // ---- main loop ------------------------------------------------------------
