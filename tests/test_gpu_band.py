@@ -219,3 +219,47 @@ def test_exchange_one_rank_writes_only_its_slot(gpu_lib):
         got = outs[u].cpu().numpy()
         assert np.array_equal(got[rank], x[u])
         assert np.all(np.delete(got, rank, axis=0) == 0xAB)
+
+
+def test_head_chunk_schedule_on_three_streams_matches_one_stream(gpu_lib):
+    """The pages' overlapped head-chunk schedule (input pack of chunk N+1,
+    consumer of chunk N and output side of chunk N-1 on three streams joined
+    by events) must give exactly the one-stream result: every entry point
+    enqueues on the stream it is given."""
+    wl = case(70, 1, 96, 16, 4, (1, 2, 1))
+    U, S, B, hl, Sg = wl.world, wl.s_local, wl.batch, wl.local_heads, wl.s_global
+    q, k, v = (to_dev(t) for t in W.rank_shards(wl)[:3])
+    sched = W.schedule_pairs(wl.schedule)
+
+    def run(streams):
+        slots = {c: [poison_dev((B, Sg, c, 384)) for _ in range(U)] for _, c in sched}
+        bands = {c: poison_dev((B, Sg, c, 128)) for _, c in sched}
+        recv = {c: [poison_dev((B, S, U * c, 128)) for _ in range(U)] for _, c in sched}
+        out = poison_dev((B, S, wl.heads, 128))
+        torch.cuda.synchronize()
+        s_in, s_att, s_out = streams
+        for i, (off, c) in enumerate(sched):
+            gpu_lib.ulysses_pack_qkv_head_chunk(q, k, v, world=U, schedule=wl.schedule, chunk=i,
+                                                dst=slots[c], row_offset=wl.rank * S, stream=s_in)
+            e_in = torch.cuda.Event()
+            e_in.record(s_in)
+            s_att.wait_event(e_in)
+            with torch.cuda.stream(s_att):          # stand-in consumer: the V band
+                bands[c].copy_(slots[c][0][..., 256:])
+            e_att = torch.cuda.Event()
+            e_att.record(s_att)
+            s_out.wait_event(e_att)
+            gpu_lib.ulysses_pack_output_sequence_chunk(bands[c], world=U, dst=recv[c],
+                                                       head_offset=wl.rank * c, stream=s_out)
+            gpu_lib.ulysses_merge_output_head_chunk(
+                [recv[c][0][:, :, u * c:(u + 1) * c] for u in range(U)], world=U,
+                local_heads=hl, schedule=wl.schedule, chunk=i, out=out, stream=s_out)
+        torch.cuda.synchronize()
+        return to_bits(out)
+
+    main = torch.cuda.current_stream()
+    seq = run((main, main, main))
+    par = run((torch.cuda.Stream(), torch.cuda.Stream(), torch.cuda.Stream()))
+    assert np.array_equal(seq, par)
+    # only this rank's band was exchanged: its heads (source 0) are all written
+    assert not np.any(seq[:, :, :hl] == O.POISON_BITS)
