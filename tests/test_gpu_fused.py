@@ -106,6 +106,9 @@ SMALL = [
     # M < one tile; a single token per batch entry
     W.custom(15, batch=5, s_local=1, heads=2, world=2, rank=1, layout="bshd",
              schedule=(1,), rope_base=1e4),
+    # one head: two K-steps per tile, N = 384 (the second tile column is half empty)
+    W.custom(19, batch=2, s_local=37, heads=1, world=1, rank=0, layout="fused",
+             schedule=(1,), rope_base=1e4),
 ]
 
 
