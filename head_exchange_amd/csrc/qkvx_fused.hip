@@ -112,6 +112,13 @@ __device__ __forceinline__ void wait_lgkm() {
     asm volatile("s_waitcnt lgkmcnt(%0)" ::"n"(N) : "memory");
 }
 
+// ROWS_CHECKED: M < BM, so the single tile row reads X rows past M, which must
+// come from the buffer's range check (zeros).  Otherwise the last tile row and
+// the last tile column are moved back to end at M and N, so that every operand
+// row a tile reads exists; the rows (heads) it shares with the previous tile
+// are computed again with the same instruction sequence and stored again with
+// the same bits.
+template <bool ROWS_CHECKED>
 __global__ __attribute__((amdgpu_flat_work_group_size(NT, NT), amdgpu_waves_per_eu(1, 1)))
 void fused_qkv_kernel(FusedArgs a) {
     // K-step g of the stream occupies W half 2g and X half 2g + 1; half h
@@ -149,7 +156,9 @@ void fused_qkv_kernel(FusedArgs a) {
     // With readiness words the order is destination-major: the tiles holding
     // destination d's heads (dest_cols columns in each of q, k, v) come before
     // those of d + 1, so early destinations are complete early.
-    auto tile_origin = [&](int l, int& m0, int& n0) {
+    // n_own: the first output column the tile is responsible for (before the
+    // move back), which decides the heads it counts in the readiness words.
+    auto tile_origin = [&](int l, int& m0, int& n0, int& n_own) {
         int tm, tn;
         if (a.ready && a.dest_cols > 0) {
             const int per_dest = a.tiles_m * 3 * a.dest_cols;
@@ -163,6 +172,9 @@ void fused_qkv_kernel(FusedArgs a) {
         }
         m0 = tm * BM;
         n0 = tn * BN;
+        n_own = n0;
+        if (!ROWS_CHECKED && m0 + BM > a.M) m0 = a.M - BM;
+        if (n0 + BN > a.N) n0 = a.N - BN;
     };
 
     // ---- global -> LDS: direct loads (buffer_load ... lds) ----------------------
@@ -228,10 +240,10 @@ void fused_qkv_kernel(FusedArgs a) {
     const int KT = K / BK;
     // Panels of the current tile and of this workgroup's next tile; past its
     // last tile the "next" requests re-read the current tile (in bounds, unused).
-    int m0, n0, m0_next, n0_next;
-    tile_origin(first, m0, n0);
+    int m0, n0, m0_next, n0_next, own, own_next;
+    tile_origin(first, m0, n0, own);
     int next = first + stride;
-    tile_origin(next < end ? next : first, m0_next, n0_next);
+    tile_origin(next < end ? next : first, m0_next, n0_next, own_next);
     uint32_t gw_cur = panel_offset(n0), gx_cur = panel_offset(m0);
     uint32_t gw_nxt = panel_offset(n0_next), gx_nxt = panel_offset(m0_next);
 
@@ -242,15 +254,18 @@ void fused_qkv_kernel(FusedArgs a) {
         const uint32_t g0 = is_w ? (nx ? gw_nxt : gw_cur) : (nx ? gx_nxt : gx_cur);
         const uint32_t kb = uint32_t(nx ? kidx - KT : kidx) * BK * 2u;
         const uint32_t flip = (i & 1) ? 64u : 0u;
+        const uint32_t roff = uint32_t(32 * i) * rowbytes;
         lds_uint4* dst = ring3 + buf * BUF_CHUNKS + (4 * i + wv) * 64;
-        // The row goes into the VGPR offset, which the buffer's range check
-        // covers (rows past M or N read as zero); only the K offset within a
-        // row, which keeps an in-range row in range, goes into the SGPR
-        // offset, which the check leaves out.
+        // The buffer's range check covers the VGPR offset but not the SGPR
+        // offset.  When rows past M are read (ROWS_CHECKED) the row goes into
+        // the VGPR offset so that they read as zeros; otherwise every row read
+        // exists and the instruction's row step rides in the SGPR offset with
+        // the K offset, which keeps the loop free of address arithmetic.
+        const uint32_t voff = ROWS_CHECKED ? (g0 ^ flip) + roff : (g0 ^ flip);
+        const uint32_t soff = ROWS_CHECKED ? kb : roff + kb;
         __builtin_amdgcn_raw_ptr_buffer_load_lds(is_w ? rw : rx,
                                                  (__attribute__((address_space(3))) void*)dst, 16,
-                                                 (g0 ^ flip) + uint32_t(32 * i) * rowbytes, kb,
-                                                 0, 0);
+                                                 voff, soff, 0, 0);
     };
 
     // ---- main loop ------------------------------------------------------------
@@ -452,7 +467,7 @@ void fused_qkv_kernel(FusedArgs a) {
                 __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
                 if (lane < 2) {
                     const int ncol = n0 + lane * 128;
-                    if (ncol < a.N) {
+                    if (ncol < a.N && ncol >= own) {
                         const int p = ncol / a.hidden;
                         const int h = (ncol - p * a.hidden) >> 7;
                         __hip_atomic_fetch_add(a.ready + h / a.local_heads, 2ull,
@@ -464,10 +479,11 @@ void fused_qkv_kernel(FusedArgs a) {
         if (next >= end) break;
         m0 = m0_next;
         n0 = n0_next;
+        own = own_next;
         gw_cur = gw_nxt;
         gx_cur = gx_nxt;
         next += stride;
-        tile_origin(next < end ? next : next - stride, m0_next, n0_next);
+        tile_origin(next < end ? next : next - stride, m0_next, n0_next, own_next);
         gw_nxt = panel_offset(n0_next);
         gx_nxt = panel_offset(m0_next);
     }
@@ -505,7 +521,10 @@ hipError_t launch_fused(const FusedArgs& a_in, hipStream_t stream) {
     // other streams always find room while this grid runs
     const int cus = a.ready ? device_cus() - NXCD : device_cus();
     const int grid = tiles < cus ? tiles : cus;
-    hipLaunchKernelGGL(fused_qkv_kernel, dim3(grid), dim3(NT), 0, stream, a);
+    if (a.M < BM)
+        hipLaunchKernelGGL(fused_qkv_kernel<true>, dim3(grid), dim3(NT), 0, stream, a);
+    else
+        hipLaunchKernelGGL(fused_qkv_kernel<false>, dim3(grid), dim3(NT), 0, stream, a);
     return hipGetLastError();
 }
 
