@@ -8,7 +8,7 @@ before rounding, o = RNE_bf16(r)):
     lies within 2^-12 * max(|r|, 1) of their midpoint: the fp32 accumulation of
     the kernel landed r on the other side of a rounding boundary.  Above |o| = 4
     one bf16 step is 0.03125 or more, so such a flip alone exceeds 2e-2 (the
-    pages meet the same case and classify those elements, "max_abs 0.03125").
+    pages meet the same case and classify those elements by a max-abs of one bf16 step at 4).
     Flips must stay under 1 % of the elements with |o| >= 4 (a systematic
     rounding error would flip about half);
   * every other element fails;
