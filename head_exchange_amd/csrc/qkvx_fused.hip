@@ -519,7 +519,8 @@ hipError_t launch_fused(const FusedArgs& a_in, hipStream_t stream) {
     const int tiles = a.tiles_m * a.tiles_n;
     // with readiness words one CU per XCD stays free, so that wait kernels on
     // other streams always find room while this grid runs
-    const int cus = a.ready ? device_cus() - NXCD : device_cus();
+    const int all_cus = device_cus();
+    const int cus = a.ready && all_cus > 2 * NXCD ? all_cus - NXCD : all_cus;
     const int grid = tiles < cus ? tiles : cus;
     if (a.M < BM)
         hipLaunchKernelGGL(fused_qkv_kernel<true>, dim3(grid), dim3(NT), 0, stream, a);
