@@ -47,6 +47,8 @@ def parse():
                    help="do not time the CPU oracle (for profiler runs)")
     p.add_argument("--cpu-seconds", type=float, default=12.0,
                    help="target duration of the CPU oracle sample")
+    p.add_argument("--skip-sweep", action="store_true",
+                   help="do not time the other workloads and the cold-cache launches")
     p.add_argument("--copy-calibration", action="store_true",
                    help="also run a plain 1 GiB device copy (counter calibration)")
     return p.parse_args()
@@ -121,6 +123,158 @@ def cpu_baseline(wl, x, w, wq, wk, cs, qkv_src, band, target_s: float):
             "seconds": round(dt, 2), "tokens": T}
 
 
+MFMA_FILE = os.path.join(ROOT, "profiles", "fused_qkvx_h56_u4_mfma.txt")
+SWEEP = ["h32_u4_fused", "h56_u4", "h56_u2_fused", "h48_u8_stress"]
+EVICT_BYTES = 1 << 30           # > the 256 MB MALL and the 8 x 4 MB L2s
+
+
+def read_mfma_counters():
+    """MFMA busy fraction and shader clock of the fused kernel from the committed
+    counter summary, or None when it is missing or the kernel changed since."""
+    if not os.path.exists(MFMA_FILE):
+        return None
+    text = open(MFMA_FILE).read()
+    if source_hash(FUSED_SOURCE) not in text:
+        return None
+    kv = {}
+    for line in text.splitlines():
+        if ":" in line and not line.startswith("#"):
+            k, v = line.split(":", 1)
+            kv[k.strip()] = v.strip().split()[0]
+    try:
+        return {"mfma_busy_frac": float(kv["mfma_busy_fraction"]),
+                "clock_ghz": float(kv["clock_ghz"])}
+    except (KeyError, ValueError):
+        return None
+
+
+def pct(ms):
+    """Median and 10th/90th percentiles of per-launch times, in microseconds."""
+    a = np.asarray(ms, dtype=np.float64) * 1e3
+    return {"p10_us": float(np.percentile(a, 10)), "median_us": float(np.median(a)),
+            "p90_us": float(np.percentile(a, 90))}
+
+
+def launch_times(torch, fn, reps: int, stream, lead, evict=None):
+    """Per-launch times (ms) from HIP events recorded on the launch stream around
+    each launch.  With ``evict`` (a 1 GiB device buffer) each launch is preceded
+    by a fill of that buffer, so its inputs start outside the MALL and L2s.  A
+    lead fill of ``lead`` queues ahead of the first launch so that the host stays
+    ahead of the device and no enqueue latency falls between a launch's events."""
+    fn()
+    torch.cuda.synchronize()
+    lead.fill_(0)
+    evs = []
+    for i in range(reps):
+        if evict is not None:
+            evict.fill_(i & 0xFF)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        fn()
+        e1.record(stream)
+        evs.append((e0, e1))
+    torch.cuda.synchronize()
+    return [a.elapsed_time(b) for a, b in evs]
+
+
+def device_normal(torch, dev, shape, std: float, seed: int):
+    """Seeded N(0, std) bf16 drawn on the device (torch's Philox generator), for
+    timing inputs only: same shapes and distributions as the workload recipe."""
+    g = torch.Generator(device=dev)
+    g.manual_seed(seed)
+    return (torch.randn(shape, generator=g, device=dev, dtype=torch.float32) * std).to(
+        torch.bfloat16)
+
+
+def sweep(hx, torch, W, dev, reps: int = 10):
+    """Every multi-head workload at its full size: the fused kernel, and pack and
+    merge per chunk, each timed back to back (warm) and after a 1 GiB eviction
+    fill (cold).  Rates use the algorithmic work: 2*M*N*K for the fused kernel,
+    bytes read + written by the band copy for pack and merge."""
+    stream = torch.cuda.current_stream()
+    evict = torch.empty(EVICT_BYTES, dtype=torch.uint8, device=dev)
+    out = {}
+    for name in SWEEP:
+        wl = W.WORKLOADS[name]
+        M, N, K = wl.gemm_shape
+        S, U, hl, B, H = wl.s_local, wl.world, wl.local_heads, wl.batch, wl.heads
+        sched = W.schedule_pairs(wl.schedule)
+        xs = [device_normal(torch, dev, (B, S, wl.hidden), wl.x_std, wl.seed("x", c))
+              for c in range(wl.calls)]
+        w = device_normal(torch, dev, (N, K), 1.0 / np.sqrt(K), wl.seed("w"))
+        wq_h, wk_h = W.norm_weights(wl)
+        wq, wk = torch.from_numpy(wq_h).to(dev), torch.from_numpy(wk_h).to(dev)
+        cs = torch.from_numpy(W.table(wl)).to(dev)
+        sess = hx.qkvx_create(wl.hidden, H, 128, U, wl.layout, M, wl.num_slots)
+        calls = [0]
+
+        def fused():
+            sess.forward(xs[calls[0] % len(xs)], w, wq, wk, cs, wl.rank, stream)
+            calls[0] += 1
+
+        for _ in range(3):
+            fused()
+        flops = 2.0 * M * N * K
+        res = {"gemm_mnk": [M, N, K], "layout": wl.layout, "world": U,
+               "schedule": list(wl.schedule), "fused_calls_cycled": wl.calls}
+        for mode, ev in (("warm", None), ("cold", evict)):
+            st = pct(launch_times(torch, fused, reps, stream, evict, ev))
+            st["tflops"] = flops / (st["median_us"] * 1e-6) / 1e12
+            st["frac"] = st["tflops"] / PEAK_BF16_TFLOPS
+            res[f"fused_{mode}"] = st
+        sess.close()
+        del xs, w, sess
+        torch.cuda.empty_cache()
+
+        shape = (B, S, H, 128)
+        if wl.pack_source == "fused384":
+            base = device_normal(torch, dev, (B, S, H, 384), 1.0, wl.seed("qkv384"))
+            q, k, v = base[..., :128], base[..., 128:256], base[..., 256:]
+        else:
+            q, k, v = (device_normal(torch, dev, shape, 1.0, wl.seed(t)) for t in "qkv")
+        band = device_normal(torch, dev, (B, wl.s_global, hl, 128), 1.0, wl.seed("band"))
+        srcs = [band[:, u * S:(u + 1) * S] for u in range(U)]
+        mout = torch.empty(shape, dtype=torch.bfloat16, device=dev)
+        chunks = []
+        for c, (off, cnt) in enumerate(sched):
+            dst = [torch.empty(B, wl.s_global, cnt, 384, dtype=torch.bfloat16, device=dev)
+                   for _ in range(U)]
+            cases = {
+                "pack": (lambda c=c, dst=dst: hx.ulysses_pack_qkv_head_chunk(
+                    q, k, v, world=U, schedule=wl.schedule, chunk=c, dst=dst,
+                    row_offset=wl.rank * S, stream=stream), 2.0 * B * S * U * cnt * 384 * 2),
+                "merge": (lambda c=c, off=off: hx.ulysses_merge_output_head_chunk(
+                    srcs, world=U, local_heads=hl, schedule=wl.schedule, chunk=c, out=mout,
+                    head_offset=off, stream=stream), 2.0 * B * S * U * cnt * 128 * 2),
+            }
+            row = {"heads": cnt}
+            for kind, (fn, nbytes) in cases.items():
+                row[f"{kind}_bytes"] = nbytes
+                for mode, ev in (("warm", None), ("cold", evict)):
+                    st = pct(launch_times(torch, fn, reps, stream, evict, ev))
+                    st["gbps"] = nbytes / (st["median_us"] * 1e-6) / 1e9
+                    st["frac"] = st["gbps"] / PEAK_HBM_GBPS
+                    row[f"{kind}_{mode}"] = st
+            chunks.append(row)
+            del dst
+        res["chunks"] = chunks
+        for kind in ("pack", "merge"):
+            for mode in ("warm", "cold"):
+                nbytes = sum(r[f"{kind}_bytes"] for r in chunks)
+                us = sum(r[f"{kind}_{mode}"]["median_us"] for r in chunks)
+                res[f"{kind}_{mode}_all_chunks"] = {
+                    "us": us, "gbps": nbytes / (us * 1e-6) / 1e9,
+                    "frac": nbytes / (us * 1e-6) / 1e9 / PEAK_HBM_GBPS}
+        out[name] = res
+        del q, k, v, band, srcs, mout
+        if wl.pack_source == "fused384":
+            del base
+        torch.cuda.empty_cache()
+    del evict
+    torch.cuda.empty_cache()
+    return out
+
+
 def output_side(hx, torch, wl, band, sched, dev, reps: int = 10):
     """Times the whole-band and output-side transforms of one rank on the same
     shard (outside the step): scatter_heads of a [B, S_local, H, 128] input,
@@ -130,14 +284,14 @@ def output_side(hx, torch, wl, band, sched, dev, reps: int = 10):
     algorithmic: every element read once and written once."""
     S, U, hl, B = wl.s_local, wl.world, wl.local_heads, wl.batch
     stream = torch.cuda.current_stream()
-    shard = torch.empty(B, S, wl.heads, 128, dtype=torch.bfloat16, device=dev).normal_()
+    shard = device_normal(torch, dev, (B, S, wl.heads, 128), 1.0, wl.seed("shard"))
     scat = [torch.empty(B, wl.s_global, hl, 128, dtype=torch.bfloat16, device=dev)
             for _ in range(U)]
     gath = [torch.empty(B, S, wl.heads, 128, dtype=torch.bfloat16, device=dev) for _ in range(U)]
     staging = [torch.empty(U, B, S, cnt, 128, dtype=torch.bfloat16, device=dev)
                for _, cnt in sched]
     msg = B * S * hl * 384 * 2
-    ex_x = torch.empty(U, msg, dtype=torch.uint8, device=dev).random_(0, 256)
+    ex_x = device_normal(torch, dev, (U, msg // 2), 1.0, wl.seed("chunks")).view(torch.uint8)
     ex_out = [torch.empty(U, msg, dtype=torch.uint8, device=dev) for _ in range(U)]
     cases = {
         "scatter_heads": (lambda: hx.ulysses_scatter_heads(shard, world=U, dst=scat,
@@ -374,9 +528,9 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
 
-    fused_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in events]))
-    pack_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in events]))
-    merge_ms = float(np.mean([e[2].elapsed_time(e[3]) for e in events]))
+    per = {name: [e[a].elapsed_time(e[a + 1]) for e in events]
+           for a, name in enumerate(("fused", "pack_all_chunks", "merge_all_chunks"))}
+    fused_ms, pack_ms, merge_ms = (float(np.mean(per[n])) for n in per)
     step_ms = wall * 1e3 / args.steps
     flops = 2.0 * M * N * K
     pack_bytes = sum(2.0 * B * S * U * cnt * 384 * 2 for _, cnt in sched)
@@ -427,10 +581,18 @@ def main():
                       "pack_bytes": pack_bytes, "merge_bytes": merge_bytes,
                       "peak_gbps": PEAK_HBM_GBPS},
         "kernels_ms": {"fused": fused_ms, "pack_all_chunks": pack_ms, "merge_all_chunks": merge_ms},
+        "kernels_pct": {n: pct(v) for n, v in per.items()},
     }
+    counters = read_mfma_counters()
+    if counters:
+        result["roofline"].update(counters)
     result["output_side"] = output_side(hx, torch, wl, band, sched, dev)
     result["readiness"] = readiness(hx, torch, wl, x, w, wq, wk, cs, dev)
     result["head_chunk_pipeline"] = head_chunk_pipeline(hx, torch, wl, q, k, v, sched, dev)
+    if not args.skip_sweep:
+        del q, k, v, band, pack_dst, merge_out, merge_src
+        torch.cuda.empty_cache()
+        result["sweep"] = sweep(hx, torch, W, dev)
     if calib:
         result["copy_calibration"] = calib
     if not args.skip_cpu_baseline:

@@ -133,25 +133,50 @@ void fused_qkv_kernel(FusedArgs a) {
 
     // ---- tile schedule ---------------------------------------------------------
     // XCD x (workgroups b with b % 8 == x) owns a contiguous eighth of the
-    // logical tile order; its G/8 workgroups walk that range G/8 tiles at a
-    // time.  With readiness words the whole grid walks the order together
-    // instead (tile b + G i), so that destinations complete one after another.
+    // logical tile order.  Its G/8 workgroups take the first two G/8-tile
+    // rounds of that range in a fixed order; with tile-claim counters the rest
+    // is claimed one tile at a time (the counter of XCD x first, then those of
+    // the other XCDs once x's range is used up), so that XCDs running at a
+    // higher clock take more tiles and all finish together.  Without counters
+    // the workgroups walk the whole range G/8 tiles at a time.  With readiness
+    // words the whole grid walks the order together instead (tile b + G i),
+    // so that destinations complete one after another.
     const int G = gridDim.x;
     const int bid = blockIdx.x;
     const int total = a.tiles_m * a.tiles_n;
+    const bool by_xcd = G % NXCD == 0 && !a.ready;
+    const bool claim = by_xcd && a.sched != nullptr;
+    const int per = total / NXCD, rem = total % NXCD;
+    auto range_start = [&](int x) { return x * per + min(x, rem); };
+    auto range_len = [&](int x) { return per + (x < rem ? 1 : 0); };
+    const int xcd = bid % NXCD;
     int first, stride, end;
-    if (G % NXCD == 0 && !a.ready) {
-        const int x = bid % NXCD;
-        const int per = total / NXCD, rem = total % NXCD;
-        first = x * per + min(x, rem) + bid / NXCD;
-        end = (x + 1) * per + min(x + 1, rem);
+    if (by_xcd) {
+        first = range_start(xcd) + bid / NXCD;
+        end = range_start(xcd) + range_len(xcd);
         stride = G / NXCD;
     } else {
         first = bid;
         end = total;
         stride = G;
     }
-    if (first >= end) return;
+    // Once a workgroup has claimed its last tile it counts itself finished;
+    // the last one to do so zeroes the counters for the next launch (every
+    // claim of this launch has returned by then).
+    auto finish = [&]() {
+        if (claim && threadIdx.x == 0) {
+            const unsigned int old = __hip_atomic_fetch_add(a.sched + NXCD, 1u, __ATOMIC_RELAXED,
+                                                            __HIP_MEMORY_SCOPE_AGENT);
+            if (old == unsigned(G - 1)) {
+                for (int v = 0; v <= NXCD; ++v)
+                    __hip_atomic_store(a.sched + v, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            }
+        }
+    };
+    if (first >= end) {
+        finish();
+        return;
+    }
     const int K = a.K;
     // With readiness words the order is destination-major: the tiles holding
     // destination d's heads (dest_cols columns in each of q, k, v) come before
@@ -240,10 +265,11 @@ void fused_qkv_kernel(FusedArgs a) {
     const int KT = K / BK;
     // Panels of the current tile and of this workgroup's next tile; past its
     // last tile the "next" requests re-read the current tile (in bounds, unused).
+    // nxt: the tile after the current one, or -1.
     int m0, n0, m0_next, n0_next, own, own_next;
     tile_origin(first, m0, n0, own);
-    int next = first + stride;
-    tile_origin(next < end ? next : first, m0_next, n0_next, own_next);
+    int nxt = first + stride < end ? first + stride : -1;
+    tile_origin(nxt >= 0 ? nxt : first, m0_next, n0_next, own_next);
     uint32_t gw_cur = panel_offset(n0), gx_cur = panel_offset(m0);
     uint32_t gw_nxt = panel_offset(n0_next), gx_nxt = panel_offset(m0_next);
 
@@ -438,6 +464,10 @@ void fused_qkv_kernel(FusedArgs a) {
     }
   };
 
+    // claim state (thread 0 only): the XCD counter being drawn from, and how
+    // many counters were found used up
+    int cvict = xcd, ctried = 0;
+
     // prologue: W and X halves of K-step 0 and the W half of K-step 1
 #pragma unroll
     for (int i = 0; i < HLOADS; ++i) load_one(true, i, 0, 0);
@@ -457,6 +487,13 @@ void fused_qkv_kernel(FusedArgs a) {
         // the nops give the last MFMAs' results the wait states an accumulator
         // read needs
         asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
+        // Claim the tile after nxt: the counter's reply is only needed after
+        // the epilogue, whose own memory waits cover it.
+        const bool claiming = claim && nxt >= 0;
+        unsigned int reply = 0;
+        if (claiming && threadIdx.x == 0)
+            reply = __hip_atomic_fetch_add(a.sched + cvict, 1u, __ATOMIC_RELAXED,
+                                           __HIP_MEMORY_SCOPE_AGENT);
         epilogue(m0, n0);
         if (a.ready) {
             // publish: once all four waves' stores of this tile are complete,
@@ -476,17 +513,50 @@ void fused_qkv_kernel(FusedArgs a) {
                 }
             }
         }
-        if (next >= end) break;
+        if (nxt < 0) break;
+        int after;
+        if (claiming) {
+            // Thread 0 turns the reply into a tile (claiming from the next
+            // XCDs' counters while the current one's range is used up) and
+            // hands it to the other waves through the first word of the buffer
+            // the last K-step's W half used: it is free until the next tile's
+            // first step loads into it, after the second barrier.
+            const uint32_t mail = ring0 + uint32_t(pw >= 2 ? pw - 2 : pw + 3) * (BUF_CHUNKS * 16);
+            if (threadIdx.x == 0) {
+                int t = -1;
+                for (;;) {
+                    const int idx = 2 * stride + int(reply);
+                    if (idx < range_len(cvict)) {
+                        t = range_start(cvict) + idx;
+                        break;
+                    }
+                    if (++ctried == NXCD) break;
+                    cvict = cvict == NXCD - 1 ? 0 : cvict + 1;
+                    reply = __hip_atomic_fetch_add(a.sched + cvict, 1u, __ATOMIC_RELAXED,
+                                                   __HIP_MEMORY_SCOPE_AGENT);
+                }
+                asm volatile("ds_write_b32 %0, %1\n\ts_waitcnt lgkmcnt(0)" ::"v"(mail), "v"(t)
+                             : "memory");
+            }
+            int got;
+            asm volatile("s_barrier\n\tds_read_b32 %0, %1\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier"
+                         : "=v"(got) : "v"(mail) : "memory");
+            after = __builtin_amdgcn_readfirstlane(got);
+        } else {
+            after = nxt + stride < end ? nxt + stride : -1;
+        }
         m0 = m0_next;
         n0 = n0_next;
         own = own_next;
         gw_cur = gw_nxt;
         gx_cur = gx_nxt;
-        next += stride;
-        tile_origin(next < end ? next : next - stride, m0_next, n0_next, own_next);
+        // past the last tile the "next" requests re-read the current one
+        tile_origin(after >= 0 ? after : nxt, m0_next, n0_next, own_next);
+        nxt = after;
         gw_nxt = panel_offset(n0_next);
         gx_nxt = panel_offset(m0_next);
     }
+    finish();
     // drain the requests of the (non-existent) tile after the last one before
     // the workgroup's LDS can be handed to another workgroup
     asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");

@@ -147,6 +147,7 @@ struct qkvx_session {
     bool last_published;               // the last call did
     unsigned long long* ready;         // device: QKVX_MAX_WORLD readiness words
     int* timeouts;                     // device: wait-kernel timeout counter
+    unsigned int* sched;               // device: tile-claim counters (first forward call)
     unsigned long long expect[QKVX_MAX_WORLD];   // word values after the last publishing call
     int64_t calls;              // successful forward calls so far
     bool has_last;
@@ -231,6 +232,7 @@ int qkvx_create(int hidden, int num_heads, int head_dim, int world, int layout, 
     s->last_published = false;
     s->ready = nullptr;
     s->timeouts = nullptr;
+    s->sched = nullptr;
     memset(s->expect, 0, sizeof(s->expect));
     *out = s;
     return ok();
@@ -239,6 +241,7 @@ int qkvx_create(int hidden, int num_heads, int head_dim, int world, int layout, 
 int qkvx_destroy(qkvx_session* s) {
     if (!s) return fail(QKVX_ERR_INVALID, "session is NULL");
     if (s->ready) hipFree(s->ready);
+    if (s->sched) hipFree(s->sched);
     if (s->owns_slots) {
         hipError_t e = hipFree(s->slots);
         delete s;
@@ -341,6 +344,20 @@ int qkvx_forward(qkvx_session* s, const void* x, int batch, int s_local, const v
         const int hl = s->heads / s->world;
         a.dest_cols = (hl % 2 == 0 && hidden % 256 == 0) ? hl / 2 : 0;
         a.part_cols = int32_t(hidden / 256);
+    } else {
+        if (!s->sched) {
+            // zeroed once, synchronously; every launch leaves them zero again
+            void* mem = nullptr;
+            hipError_t e = hipMalloc(&mem, kSchedWords * sizeof(unsigned int));
+            if (e == hipSuccess) e = hipMemset(mem, 0, kSchedWords * sizeof(unsigned int));
+            if (e == hipSuccess) e = hipDeviceSynchronize();
+            if (e != hipSuccess) {
+                if (mem) hipFree(mem);
+                return hip_fail(e, "allocation of the tile-claim counters");
+            }
+            s->sched = static_cast<unsigned int*>(mem);
+        }
+        a.sched = s->sched;
     }
     hipError_t e = launch_fused(a, static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return hip_fail(e, "fused projection launch");

@@ -70,7 +70,14 @@ struct FusedArgs {
     unsigned long long* ready;
     int32_t dest_cols;        // 256-column tiles per destination and part (H_local / 2)
     int32_t part_cols;        // 256-column tiles per part (hidden / 256)
+    // Tile-claim counters (null: every workgroup walks a fixed share of the
+    // tiles).  Words 0-7: tiles claimed beyond the fixed ones in each XCD's
+    // range; word 8: workgroups finished.  Zero before a launch; the last
+    // workgroup to finish zeroes them again.  Not used with readiness words.
+    unsigned int* sched;
 };
+
+constexpr int kSchedWords = 16;   // tile-claim counter words a session keeps
 
 // Readiness: a call adds this much to ready[d] of every destination d.
 inline unsigned long long ready_increment(int64_t M, int local_heads) {

@@ -240,3 +240,38 @@ def test_describe_and_last_outputs(gpu_lib):
     assert last[1][2].data_ptr() == views[1][2].data_ptr()
     assert json.loads(sess.describe())["next_slot"] == 1
     sess.close()
+
+
+# 63 x 12 = 756 tiles (ragged last tile row): more than two tiles per workgroup,
+# so most XCD ranges are finished by claimed tiles.
+CLAIMED = W.custom(20, batch=4, s_local=4000, heads=8, world=2, rank=1, layout="bshd",
+                   schedule=(2, 2), rope_base=1e4)
+
+
+def test_claimed_tiles_cover_every_tile_on_every_call(gpu_lib):
+    """With tile claiming, every call writes every row of the rank (checked
+    whole against the oracle on the first call), later calls reproduce the
+    first bit for bit (the claim counters start from zero each time), and the
+    fixed destination-major order of a publishing session gives the same
+    bits: which workgroup computes a tile does not change its values."""
+    wl = CLAIMED
+    inp = Inputs(wl)
+    sess = make_session(gpu_lib, wl)
+    assert -(-wl.tokens // 256) * (3 * wl.hidden // 256) > 2 * 256
+    sess.poison_receive_slots()
+    views = run(sess, inp)
+    torch.cuda.synchronize()
+    check_full(views, inp, wl.rank, "claimed:call0")
+    first = slot_full(views, wl.layout)
+    for call in (1, 2, 3):
+        sess.poison_receive_slots()
+        got = slot_full(run(sess, inp), wl.layout)
+        for d in range(wl.world):
+            assert np.array_equal(got[d], first[d]), f"call {call} dest {d} differs"
+    pub = make_session(gpu_lib, wl)
+    pub.set_publish(True)
+    pub.poison_receive_slots()
+    got = slot_full(run(pub, inp), wl.layout)
+    for d in range(wl.world):
+        assert np.array_equal(got[d], first[d]), f"publishing order dest {d} differs"
+    assert pub.ready_state() == (pub.ready_expected(), 0)
