@@ -107,6 +107,44 @@ __device__ __forceinline__ float acc_read(const float& a) {
     return v;
 }
 
+// Lane exchange within groups of four lanes (DPP quad permutation).
+template <int CTRL>
+__device__ __forceinline__ uint32_t quad_perm(uint32_t v) {
+    return uint32_t(__builtin_amdgcn_mov_dpp(int(v), CTRL, 0xF, 0xF, false));
+}
+constexpr int kQuadSwap2 = 2 | 3 << 2 | 0 << 4 | 1 << 6;   // lane k reads lane k ^ 2
+constexpr int kQuadSwap1 = 1 | 0 << 2 | 3 << 4 | 2 << 6;   // lane k reads lane k ^ 1
+template <int I>
+constexpr int quad_bcast() { return I | I << 2 | I << 4 | I << 6; }   // every lane reads lane I
+
+// Transpose of 4 x 4 elements of 16 bytes within each group of four lanes:
+// on entry lane k holds pieces r[0..3] of its own row, on return r[i] holds
+// piece k of the row of lane i of the group.  Two exchange stages, between
+// lanes k and k ^ 2 (pieces with bit 1 set) and between k and k ^ 1 (bit 0).
+__device__ __forceinline__ void quad_transpose(uint4 (&r)[4], int k) {
+    const bool b1 = (k >> 1) & 1, b0 = k & 1;
+#pragma unroll
+    for (int jj = 0; jj < 2; ++jj) {
+        uint32_t* lo = reinterpret_cast<uint32_t*>(&r[jj]);
+        uint32_t* hi = reinterpret_cast<uint32_t*>(&r[jj + 2]);
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            const uint32_t recv = quad_perm<kQuadSwap2>(b1 ? lo[c] : hi[c]);
+            if (b1) lo[c] = recv; else hi[c] = recv;
+        }
+    }
+#pragma unroll
+    for (int jj = 0; jj < 4; jj += 2) {
+        uint32_t* lo = reinterpret_cast<uint32_t*>(&r[jj]);
+        uint32_t* hi = reinterpret_cast<uint32_t*>(&r[jj + 1]);
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            const uint32_t recv = quad_perm<kQuadSwap1>(b0 ? lo[c] : hi[c]);
+            if (b0) lo[c] = recv; else hi[c] = recv;
+        }
+    }
+}
+
 template <int N>
 __device__ __forceinline__ void wait_lgkm() {
     asm volatile("s_waitcnt lgkmcnt(%0)" ::"n"(N) : "memory");
@@ -118,7 +156,7 @@ __device__ __forceinline__ void wait_lgkm() {
 // row a tile reads exists; the rows (heads) it shares with the previous tile
 // are computed again with the same instruction sequence and stored again with
 // the same bits.
-template <bool ROWS_CHECKED>
+template <bool ROWS_CHECKED, bool ROPE_IL>
 __global__ __attribute__((amdgpu_flat_work_group_size(NT, NT), amdgpu_waves_per_eu(1, 1)))
 void fused_qkv_kernel(FusedArgs a) {
     // K-step g of the stream occupies W half 2g and X half 2g + 1; half h
@@ -364,6 +402,12 @@ void fused_qkv_kernel(FusedArgs a) {
     // 2h+1 continue each other (16 bytes of bf16); n-block nb+2 holds e + 64.
     // Each m-block is read twice (sum of squares, then the outputs, four dims
     // per n-block at a time), which keeps the VGPRs in use small.
+    //
+    // Memory: the norm weights and cos/sin values of (m-block, q) are loaded
+    // while the previous q is computed; an m-block's stores go out after the
+    // next block's first loads.  Vector memory operations retire in order, so
+    // a wait for loads also waits for every older store: stores are therefore
+    // grouped (one group per m-block) and made of whole 64-byte runs.
     auto epilogue = [&](int m0, int n0) {
     const int ncol = n0 + wn * 128;
     if (ncol >= a.N) return;
@@ -373,95 +417,184 @@ void fused_qkv_kernel(FusedArgs a) {
     const int j = h - d * a.local_heads;
     uint16_t* dbase = a.slot + int64_t(d) * a.region_elems + int64_t(p) * a.part_stride +
                       int64_t(j) * a.stride_h;
-    const bool qk = p < 2;
-    const float* nw = p == 0 ? a.wq : a.wk;
-
-#pragma unroll
-    for (int mb = 0; mb < 4; ++mb) {
-        // tokens past M (ragged last tile) are computed on token M - 1 and not stored
+    // token of m-block mb: tokens past M (ragged last tile) are computed on
+    // token M - 1 and not stored
+    auto token_row = [&](int mb, bool& in_range) {
         const int m_tile = m0 + wm * 128 + mfma_row(mb, fr);
-        const bool in_range = m_tile < a.M;
+        in_range = m_tile < a.M;
         const int m = in_range ? m_tile : a.M - 1;
         const int bidx = m / a.s_local;
         const int s = m - bidx * a.s_local;
-        const int row = a.row0 + s;                 // sequence row == position
-        uint16_t* orow = dbase + int64_t(bidx) * a.stride_b + int64_t(row) * a.stride_s;
-        const float* csr = a.cs + int64_t(row) * 128;
-        float inv = 1.f;
-        if (qk) {
-            // RMSNorm over the head's 128 values: 64 here, 64 in lane ^ 32
-            float ss = 0.f;
+        return make_int2(bidx, a.row0 + s);   // batch, sequence row == position
+    };
+    // Stores of one m-block.  Lane (fr, hf) holds 16-byte pieces q = 0..3 of
+    // dims 64 hh + 32 hf + 8 q of its token; after a transpose within each
+    // group of four lanes (four tokens), store i of a group writes the four
+    // pieces of one token's 64 contiguous bytes, so that each store makes 16
+    // requests of 64 bytes instead of 64 of 16.
+    auto store_block = [&](uint16_t* orow, bool in_range, const uint4* out) {
+        const int k = fr & 3;
+        uint4 r[2][4];
 #pragma unroll
-            for (int nb = 0; nb < 4; ++nb)
+        for (int hh = 0; hh < 2; ++hh) {
 #pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const float t = acc_read(acc[nb][mb][r]);
-                    ss += t * t;
-                }
-            ss += __shfl_xor(ss, 32);
-            inv = rsqrtf(ss * (1.0f / 128.0f) + a.eps);
+            for (int q = 0; q < 4; ++q) r[hh][q] = out[2 * q + hh];
+            quad_transpose(r[hh], k);
         }
+        // store i: the row of group lane i (its pointer and range flag read
+        // from that lane), this lane's piece k
+        const uint64_t rowp = reinterpret_cast<uint64_t>(orow);
+        const uint32_t rlo = uint32_t(rowp), rhi = uint32_t(rowp >> 32), ok = in_range;
+        const uint64_t off = uint64_t(64 * hf + 16 * k);          // bytes
+        auto put = [&](uint32_t lo, uint32_t hi, uint32_t f, int i) {
+            if (f) {
+                uint16_t* dst = reinterpret_cast<uint16_t*>(((uint64_t(hi) << 32) | lo) + off);
+#pragma unroll
+                for (int hh = 0; hh < 2; ++hh)
+                    *reinterpret_cast<uint4*>(dst + 64 * hh) = r[hh][i];
+            }
+        };
+        put(quad_perm<quad_bcast<0>()>(rlo), quad_perm<quad_bcast<0>()>(rhi),
+            quad_perm<quad_bcast<0>()>(ok), 0);
+        put(quad_perm<quad_bcast<1>()>(rlo), quad_perm<quad_bcast<1>()>(rhi),
+            quad_perm<quad_bcast<1>()>(ok), 1);
+        put(quad_perm<quad_bcast<2>()>(rlo), quad_perm<quad_bcast<2>()>(rhi),
+            quad_perm<quad_bcast<2>()>(ok), 2);
+        put(quad_perm<quad_bcast<3>()>(rlo), quad_perm<quad_bcast<3>()>(rhi),
+            quad_perm<quad_bcast<3>()>(ok), 3);
+    };
+    auto pack = [&](const float (&v)[4][4], uint4* out2) {
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+            uint4 pk;
+            pk.x = uint32_t(bf16_bits(v[2 * hh][0])) | (uint32_t(bf16_bits(v[2 * hh][1])) << 16);
+            pk.y = uint32_t(bf16_bits(v[2 * hh][2])) | (uint32_t(bf16_bits(v[2 * hh][3])) << 16);
+            pk.z = uint32_t(bf16_bits(v[2 * hh + 1][0])) |
+                   (uint32_t(bf16_bits(v[2 * hh + 1][1])) << 16);
+            pk.w = uint32_t(bf16_bits(v[2 * hh + 1][2])) |
+                   (uint32_t(bf16_bits(v[2 * hh + 1][3])) << 16);
+            out2[hh] = pk;
+        }
+    };
+
+    if (p == 2) {
+        // V: rounding and placement only
+#pragma unroll
+        for (int mb = 0; mb < 4; ++mb) {
+            bool in_range;
+            const auto br = token_row(mb, in_range);
+            uint16_t* orow = dbase + int64_t(br.x) * a.stride_b + int64_t(br.y) * a.stride_s;
+            uint4 out[8];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                float v[4][4];
+#pragma unroll
+                for (int nb = 0; nb < 4; ++nb)
+#pragma unroll
+                    for (int g = 0; g < 4; ++g) v[nb][g] = acc_read(acc[nb][mb][q + 4 * g]);
+                pack(v, out + 2 * q);
+            }
+            store_block(orow, in_range, out);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        return;
+    }
+
+    // Per (m-block, q) the lane needs 4 weight vectors and 2 + 2 cos/sin
+    // vectors; they are loaded one q ahead into the other of two buffers.
+    //   Wq[i] = w[64 (i / 2) + 32 hf + 8 q + 4 (i % 2)]          (i < 4)
+    //   rotate-half: Cq[lo] = cs[row][32 hf + 8 q + 4 lo], Sq at + 64
+    //   interleaved: Cq[hi] = cs[row][32 hi + 16 hf + 4 q],  Sq at + 64
+    const float* nw = p == 0 ? a.wq : a.wk;
+    f32x4 Wb[2][4], Cb[2][2], Sb[2][2];
+    int rows[4];
+    bool in_range[4];
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb) {
+        const auto br = token_row(mb, in_range[mb]);
+        rows[mb] = br.y;
+    }
+    auto load_q = [&](int mb, int q, int buf) {
+        const float* csr = a.cs + int64_t(rows[mb]) * 128;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            Wb[buf][i] = *reinterpret_cast<const f32x4*>(nw + 64 * (i >> 1) + 32 * hf + 8 * q +
+                                                         4 * (i & 1));
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const int off = ROPE_IL ? 32 * i + 16 * hf + 4 * q : 32 * hf + 8 * q + 4 * i;
+            Cb[buf][i] = *reinterpret_cast<const f32x4*>(csr + off);
+            Sb[buf][i] = *reinterpret_cast<const f32x4*>(csr + 64 + off);
+        }
+    };
+    load_q(0, 0, 0);
+
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb) {
+        // RMSNorm over the head's 128 values: 64 here, 64 in lane ^ 32
+        float ss = 0.f;
+#pragma unroll
+        for (int nb = 0; nb < 4; ++nb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const float t = acc_read(acc[nb][mb][r]);
+                ss += t * t;
+            }
+        ss += __shfl_xor(ss, 32);
+        const float inv = rsqrtf(ss * (1.0f / 128.0f) + a.eps);
+        uint4 out[8];
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
+            const int cur = (4 * mb + q) & 1;
+            if (4 * mb + q < 15) load_q(q < 3 ? mb : mb + 1, (q + 1) & 3, cur ^ 1);
             // v[nb][g] = dim e(nb, q) + g, g = 0..3 (registers q + 4 g)
             float v[4][4];
 #pragma unroll
             for (int nb = 0; nb < 4; ++nb)
 #pragma unroll
                 for (int g = 0; g < 4; ++g) v[nb][g] = acc_read(acc[nb][mb][q + 4 * g]);
-            if (qk) {
-                if (a.rope_interleaved) {
-                    // pairs (2i, 2i+1) = dims (E, E+1) and (E+2, E+3) of each
-                    // n-block, E = e(nb, q), rotated by the angles of table
-                    // columns E/2 and E/2 + 1
+            if (ROPE_IL) {
+                // pairs (2i, 2i+1) = dims (E, E+1) and (E+2, E+3) of each
+                // n-block, E = e(nb, q), rotated by the angles of table columns
+                // E/2 and E/2 + 1
 #pragma unroll
-                    for (int nb = 0; nb < 4; ++nb) {
-                        const int e = 64 * (nb >> 1) + 32 * hf + 8 * q + 4 * (nb & 1);
-                        const f32x4 wt = *reinterpret_cast<const f32x4*>(nw + e);
-                        const f32x2 cv = *reinterpret_cast<const f32x2*>(csr + e / 2);
-                        const f32x2 sv = *reinterpret_cast<const f32x2*>(csr + 64 + e / 2);
+                for (int nb = 0; nb < 4; ++nb) {
+                    const f32x4 wt = Wb[cur][nb];
+                    const f32x4 cv = Cb[cur][nb >> 1], sv = Sb[cur][nb >> 1];
 #pragma unroll
-                        for (int gp = 0; gp < 2; ++gp) {
-                            const float z0 = v[nb][2 * gp] * (inv * wt[2 * gp]);
-                            const float z1 = v[nb][2 * gp + 1] * (inv * wt[2 * gp + 1]);
-                            v[nb][2 * gp] = z0 * cv[gp] - z1 * sv[gp];
-                            v[nb][2 * gp + 1] = z1 * cv[gp] + z0 * sv[gp];
-                        }
+                    for (int gp = 0; gp < 2; ++gp) {
+                        const float z0 = v[nb][2 * gp] * (inv * wt[2 * gp]);
+                        const float z1 = v[nb][2 * gp + 1] * (inv * wt[2 * gp + 1]);
+                        const float c = cv[2 * (nb & 1) + gp], sn = sv[2 * (nb & 1) + gp];
+                        v[nb][2 * gp] = z0 * c - z1 * sn;
+                        v[nb][2 * gp + 1] = z1 * c + z0 * sn;
                     }
-                } else {
-                    // rotate-half: n-blocks lo and lo + 2 hold dims e and e + 64
+                }
+            } else {
+                // rotate-half: n-blocks lo and lo + 2 hold dims e and e + 64
 #pragma unroll
-                    for (int lo = 0; lo < 2; ++lo) {
-                        const int e = 32 * hf + 8 * q + 4 * lo;
-                        const f32x4 wl = *reinterpret_cast<const f32x4*>(nw + e);
-                        const f32x4 wh = *reinterpret_cast<const f32x4*>(nw + 64 + e);
-                        const f32x4 cv = *reinterpret_cast<const f32x4*>(csr + e);
-                        const f32x4 sv = *reinterpret_cast<const f32x4*>(csr + 64 + e);
+                for (int lo = 0; lo < 2; ++lo) {
+                    const f32x4 wl = Wb[cur][lo], wh = Wb[cur][2 + lo];
+                    const f32x4 cv = Cb[cur][lo], sv = Sb[cur][lo];
 #pragma unroll
-                        for (int g = 0; g < 4; ++g) {
-                            const float zl = v[lo][g] * (inv * wl[g]);
-                            const float zh = v[lo + 2][g] * (inv * wh[g]);
-                            v[lo][g] = zl * cv[g] - zh * sv[g];
-                            v[lo + 2][g] = zh * cv[g] + zl * sv[g];
-                        }
+                    for (int g = 0; g < 4; ++g) {
+                        const float zl = v[lo][g] * (inv * wl[g]);
+                        const float zh = v[lo + 2][g] * (inv * wh[g]);
+                        v[lo][g] = zl * cv[g] - zh * sv[g];
+                        v[lo + 2][g] = zh * cv[g] + zl * sv[g];
                     }
                 }
             }
-#pragma unroll
-            for (int hh = 0; hh < 2; ++hh) {
-                const int e = 64 * hh + 32 * hf + 8 * q;
-                uint4 pk;
-                pk.x = uint32_t(bf16_bits(v[2 * hh][0])) | (uint32_t(bf16_bits(v[2 * hh][1])) << 16);
-                pk.y = uint32_t(bf16_bits(v[2 * hh][2])) | (uint32_t(bf16_bits(v[2 * hh][3])) << 16);
-                pk.z = uint32_t(bf16_bits(v[2 * hh + 1][0])) |
-                       (uint32_t(bf16_bits(v[2 * hh + 1][1])) << 16);
-                pk.w = uint32_t(bf16_bits(v[2 * hh + 1][2])) |
-                       (uint32_t(bf16_bits(v[2 * hh + 1][3])) << 16);
-                if (in_range) *reinterpret_cast<uint4*>(orow + e) = pk;
-            }
+            pack(v, out + 2 * q);
+            __builtin_amdgcn_sched_barrier(0);
         }
+        // this block's stores go out after the next block's first loads
+        const auto br = token_row(mb, in_range[mb]);
+        uint16_t* orow = dbase + int64_t(br.x) * a.stride_b + int64_t(br.y) * a.stride_s;
+        store_block(orow, in_range[mb], out);
         __builtin_amdgcn_sched_barrier(0);
     }
+    __builtin_amdgcn_sched_barrier(0);
   };
 
     // claim state (thread 0 only): the XCD counter being drawn from, and how
@@ -592,10 +725,11 @@ hipError_t launch_fused(const FusedArgs& a_in, hipStream_t stream) {
     const int all_cus = device_cus();
     const int cus = a.ready && all_cus > 2 * NXCD ? all_cus - NXCD : all_cus;
     const int grid = tiles < cus ? tiles : cus;
-    if (a.M < BM)
-        hipLaunchKernelGGL(fused_qkv_kernel<true>, dim3(grid), dim3(NT), 0, stream, a);
-    else
-        hipLaunchKernelGGL(fused_qkv_kernel<false>, dim3(grid), dim3(NT), 0, stream, a);
+    auto kernel = a.M < BM ? (a.rope_interleaved ? fused_qkv_kernel<true, true>
+                                                 : fused_qkv_kernel<true, false>)
+                           : (a.rope_interleaved ? fused_qkv_kernel<false, true>
+                                                 : fused_qkv_kernel<false, false>);
+    hipLaunchKernelGGL(kernel, dim3(grid), dim3(NT), 0, stream, a);
     return hipGetLastError();
 }
 
