@@ -170,34 +170,29 @@ void fused_qkv_kernel(FusedArgs a) {
     const int wm = wave >> 1;     // which 128 tokens of the tile
 
     // ---- tile schedule ---------------------------------------------------------
-    // XCD x (workgroups b with b % 8 == x) owns a contiguous eighth of the
-    // logical tile order.  Its G/8 workgroups take the first two G/8-tile
-    // rounds of that range in a fixed order; with tile-claim counters the rest
-    // is claimed one tile at a time (the counter of XCD x first, then those of
-    // the other XCDs once x's range is used up), so that XCDs running at a
-    // higher clock take more tiles and all finish together.  Without counters
-    // the workgroups walk the whole range G/8 tiles at a time.  With readiness
-    // words the whole grid walks the order together instead (tile b + G i),
-    // so that destinations complete one after another.
+    // The logical tile order is split into queues: one per XCD (workgroups b
+    // with b % 8 == x run on XCD x and own a contiguous eighth of the order),
+    // or a single queue over the whole order with readiness words (so that
+    // destinations complete one after another) or a grid that is not a
+    // multiple of 8.  A queue's workgroups take its first two rounds (one tile
+    // each per round) in a fixed order; with tile-claim counters the rest is
+    // claimed one tile at a time (the workgroup's own queue first, then the
+    // others once it is used up), so that XCDs running at a higher clock take
+    // more tiles and all finish together.  Without counters the workgroups
+    // walk their queue a round at a time.
     const int G = gridDim.x;
     const int bid = blockIdx.x;
     const int total = a.tiles_m * a.tiles_n;
     const bool by_xcd = G % NXCD == 0 && !a.ready;
-    const bool claim = by_xcd && a.sched != nullptr;
-    const int per = total / NXCD, rem = total % NXCD;
+    const int nq = by_xcd ? NXCD : 1;
+    const bool claim = a.sched != nullptr;
+    const int per = total / nq, rem = total % nq;
     auto range_start = [&](int x) { return x * per + min(x, rem); };
     auto range_len = [&](int x) { return per + (x < rem ? 1 : 0); };
-    const int xcd = bid % NXCD;
-    int first, stride, end;
-    if (by_xcd) {
-        first = range_start(xcd) + bid / NXCD;
-        end = range_start(xcd) + range_len(xcd);
-        stride = G / NXCD;
-    } else {
-        first = bid;
-        end = total;
-        stride = G;
-    }
+    const int xcd = by_xcd ? bid % NXCD : 0;        // the workgroup's queue
+    const int stride = by_xcd ? G / NXCD : G;       // workgroups per queue
+    const int first = range_start(xcd) + (by_xcd ? bid / NXCD : bid);
+    const int end = range_start(xcd) + range_len(xcd);
     // Once a workgroup has claimed its last tile it counts itself finished;
     // the last one to do so zeroes the counters for the next launch (every
     // claim of this launch has returned by then).
@@ -597,7 +592,7 @@ void fused_qkv_kernel(FusedArgs a) {
     __builtin_amdgcn_sched_barrier(0);
   };
 
-    // claim state (thread 0 only): the XCD counter being drawn from, and how
+    // claim state (thread 0 only): the queue counter being drawn from, and how
     // many counters were found used up
     int cvict = xcd, ctried = 0;
 
@@ -663,8 +658,8 @@ void fused_qkv_kernel(FusedArgs a) {
                         t = range_start(cvict) + idx;
                         break;
                     }
-                    if (++ctried == NXCD) break;
-                    cvict = cvict == NXCD - 1 ? 0 : cvict + 1;
+                    if (++ctried == nq) break;
+                    cvict = cvict == nq - 1 ? 0 : cvict + 1;
                     reply = __hip_atomic_fetch_add(a.sched + cvict, 1u, __ATOMIC_RELAXED,
                                                    __HIP_MEMORY_SCOPE_AGENT);
                 }

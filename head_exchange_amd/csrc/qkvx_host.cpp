@@ -344,7 +344,8 @@ int qkvx_forward(qkvx_session* s, const void* x, int batch, int s_local, const v
         const int hl = s->heads / s->world;
         a.dest_cols = (hl % 2 == 0 && hidden % 256 == 0) ? hl / 2 : 0;
         a.part_cols = int32_t(hidden / 256);
-    } else {
+    }
+    {
         if (!s->sched) {
             // zeroed once, synchronously; every launch leaves them zero again
             void* mem = nullptr;

@@ -71,9 +71,10 @@ struct FusedArgs {
     int32_t dest_cols;        // 256-column tiles per destination and part (H_local / 2)
     int32_t part_cols;        // 256-column tiles per part (hidden / 256)
     // Tile-claim counters (null: every workgroup walks a fixed share of the
-    // tiles).  Words 0-7: tiles claimed beyond the fixed ones in each XCD's
-    // range; word 8: workgroups finished.  Zero before a launch; the last
-    // workgroup to finish zeroes them again.  Not used with readiness words.
+    // tiles).  Words 0-7: tiles claimed beyond the fixed ones in each queue
+    // (one per XCD, or word 0 alone for a single queue); word 8: workgroups
+    // finished.  Zero before a launch; the last workgroup to finish zeroes
+    // them again.
     unsigned int* sched;
 };
 
