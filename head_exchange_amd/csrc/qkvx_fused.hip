@@ -39,13 +39,19 @@
 //    lgkmcnt waits: the buffer a read uses is only known at run time, and
 //    the compiler, unable to tell it from the buffers being loaded, would
 //    otherwise wait for every load in flight before each read.
-//  * Persistent: one workgroup per CU walks its share of the tiles, and the
-//    K-steps of consecutive output tiles form one continuous load stream, so
-//    the next tile's first K-steps are in flight while the current tile's
-//    epilogue runs.  The 8 XCDs (workgroup b runs on XCD b % 8) take
-//    consecutive ranges of a tile order that walks groups of tile rows column
-//    by column, so the tiles an XCD runs together share X and W panels in its
-//    L2.
+//  * Persistent: one workgroup per CU, and the K-steps of a workgroup's
+//    consecutive output tiles form one continuous load stream, so the next
+//    tile's first K-steps are in flight while the current tile's epilogue
+//    runs.  The 8 XCDs (workgroup b runs on XCD b % 8) take consecutive ranges
+//    of a tile order that walks groups of tile rows column by column, so the
+//    tiles an XCD runs together share X and W panels in its L2.  Each XCD runs
+//    at its own clock under this load, so past two fixed rounds workgroups
+//    claim tiles one at a time from per-XCD counters (then from the other
+//    XCDs' ranges), and all XCDs finish together.
+//  * Epilogue: Q/K norm and RoPE in registers, with the weights and cos/sin
+//    values loaded one q ahead; stores are transposed within groups of four
+//    lanes so that each store instruction writes whole 64-byte runs, and go
+//    out once per m-block.
 #include "qkvx_internal.h"
 
 namespace qkvx {
@@ -64,7 +70,6 @@ constexpr int HLOADS = 8;      // load instructions per wave per half step
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef float f32x2 __attribute__((ext_vector_type(2)));
 
 // 16-byte chunk index, within one buffer, of chunk c (0..7) of tile row r:
 // block r / 8 holds rows 8 (r / 8) .. + 7, 128 bytes each, with chunk c of a
