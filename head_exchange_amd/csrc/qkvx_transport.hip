@@ -12,9 +12,10 @@
 //   merge  : out[b, s, u*H_local + off + j, e] = src_u[b, R0 + s, j0 + j, e]
 //   scatter: dst_d[b, R0 + s, j0 + j, e] = x[b, s, d*H_local + j, e]
 //   gather : dst_u[b, R0 + s, j0 + j, e] = x[b, u*S_local + s, j, e]
-// The peer index (d or u) is blockIdx.y, so the peer's base pointers are
-// wave-uniform kernel arguments and no per-lane table lookup is needed; the rest
-// of the flat 16-byte-chunk index is split with precomputed 32-bit dividers.
+// The peer index (d or u) is blockIdx.y (pack) or the workgroup index modulo
+// the peer count (band copies), so the peer's base pointers are wave-uniform
+// kernel arguments and no per-lane table lookup is needed; the rest of the flat
+// 16-byte-chunk index is split with precomputed 32-bit dividers.
 // Each thread moves one 16-byte vector with nontemporal accesses (four for
 // small band copies).
 #include "qkvx_internal.h"
@@ -56,14 +57,19 @@ __global__ __launch_bounds__(kThreads) void pack_kernel(PackArgs a) {
     store_nt(dst, load_nt(src));
 }
 
-// VPT vectors per thread, kThreads * gridDim.x apart: small copies run with
-// VPT = 4 (a quarter of the workgroups to dispatch, four loads in flight per
-// thread), large ones with VPT = 1, which streams best.
+// VPT vectors per thread, kThreads * (workgroups per peer) apart: small copies
+// run with VPT = 4 (a quarter of the workgroups to dispatch, four loads in
+// flight per thread), large ones with VPT = 1, which streams best.  The peers
+// are interleaved along the grid (peer = workgroup % world): workgroups
+// dispatched together cover the same tokens of every peer, so a token's row of
+// the merged output (or of a scatter source) is written (read) in one burst
+// rather than in one pass per peer; measured 6 % faster on the 10-head merge
+// chunk of the 56-head U4 schedule.
 template <int VPT>
-__global__ __launch_bounds__(kThreads) void band_copy_kernel(BandCopyArgs a) {
-    const uint32_t y = blockIdx.y;
-    const uint32_t step = gridDim.x * kThreads;
-    const uint32_t c0 = blockIdx.x * kThreads + threadIdx.x;
+__global__ __launch_bounds__(kThreads) void band_copy_kernel(BandCopyArgs a, uint32_t world) {
+    const uint32_t y = blockIdx.x % world;
+    const uint32_t step = (gridDim.x / world) * kThreads;
+    const uint32_t c0 = (blockIdx.x / world) * kThreads + threadIdx.x;
     u32x4 v[VPT];
     uint16_t* dst[VPT];
 #pragma unroll
@@ -124,12 +130,13 @@ hipError_t launch_pack(const PackArgs& a, int world, hipStream_t stream) {
 
 hipError_t launch_band_copy(const BandCopyArgs& a, int world, hipStream_t stream) {
     if (a.total == 0) return hipSuccess;
+    const uint32_t w = uint32_t(world);
     if (a.total < (1u << 20)) {                       // under 16 MB per peer
-        dim3 grid((a.total + 4 * kThreads - 1) / (4 * kThreads), world);
-        hipLaunchKernelGGL(band_copy_kernel<4>, grid, dim3(kThreads), 0, stream, a);
+        dim3 grid(((a.total + 4 * kThreads - 1) / (4 * kThreads)) * w);
+        hipLaunchKernelGGL(band_copy_kernel<4>, grid, dim3(kThreads), 0, stream, a, w);
     } else {
-        dim3 grid((a.total + kThreads - 1) / kThreads, world);
-        hipLaunchKernelGGL(band_copy_kernel<1>, grid, dim3(kThreads), 0, stream, a);
+        dim3 grid(((a.total + kThreads - 1) / kThreads) * w);
+        hipLaunchKernelGGL(band_copy_kernel<1>, grid, dim3(kThreads), 0, stream, a, w);
     }
     return hipGetLastError();
 }
