@@ -93,20 +93,26 @@ def cpu_baseline(wl, x, w, wq, wk, cs, qkv_src, band, target_s: float):
     S, U, hl = wl.s_local, wl.world, wl.local_heads
     sched = W.schedule_pairs(wl.schedule)
 
+    parts = {}
+
     def step(T):
         t0 = time.perf_counter()
         xs = x[:, :T]
         vals = O.front_end_values(xs, w, wq, wk, cs, wl.heads, wl.rank)
         O.receive_slots(vals, U, wl.rank)
+        t1 = time.perf_counter()
         q, k, v = (a[:, :T] for a in qkv_src)
         for off, cnt in sched:
             dests = [np.empty((wl.batch, T, cnt, 384), np.uint16) for _ in range(U)]
             O.pack_qkv_head_chunk_into(q, k, v, U, off, cnt, dests, 0)
+        t2 = time.perf_counter()
         out = np.empty((wl.batch, T, wl.heads, 128), np.uint16)
         srcs = [band[:, u * S:u * S + T] for u in range(U)]
         for off, cnt in sched:
             O.merge_output_head_chunk(srcs, 0, off, U, hl, off, cnt, out)
-        return time.perf_counter() - t0
+        t3 = time.perf_counter()
+        parts.update(fused=t1 - t0, pack=t2 - t1, merge=t3 - t2)
+        return t3 - t0
 
     step(64)                                     # warm-up (allocations, BLAS threads)
     t_a, t_b = step(64), step(256)
@@ -116,7 +122,12 @@ def cpu_baseline(wl, x, w, wq, wk, cs, qkv_src, band, target_s: float):
     T = max(64, (T // 64) * 64)
     dt = step(T)
     flops = 2.0 * wl.batch * T * N * K
+    pack_bytes = sum(2.0 * wl.batch * T * U * cnt * 384 * 2 for _, cnt in sched)
+    merge_bytes = sum(2.0 * wl.batch * T * U * cnt * 128 * 2 for _, cnt in sched)
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "fused_tflops": flops / parts["fused"] / 1e12,
+            "pack_gbps": pack_bytes / parts["pack"] / 1e9,
+            "merge_gbps": merge_bytes / parts["merge"] / 1e9,
             "sample": f"first {T} of {S} tokens of the shard: float64 projection, RMSNorm, RoPE, "
                       f"bf16 rounding and receive-slot placement, plus the pack and merge index "
                       f"maps of those tokens for all {len(sched)} chunks; {dt:.1f} s wall",
