@@ -38,6 +38,7 @@ SMALL = [
     case(42, 3, 3, 6, 3, (2,)),
     case(43, 1, 33, 4, 1, (1, 3)),
     case(44, 2, 64, 56, 2, (7, 14, 7)),
+    case(45, 1, 3, 64, 64, (1,)),               # the largest group: 64 peers of one head
 ]
 FULL = W.WORKLOADS["h56_u4"]
 

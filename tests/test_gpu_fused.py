@@ -275,3 +275,16 @@ def test_claimed_tiles_cover_every_tile_on_every_call(gpu_lib):
     for d in range(wl.world):
         assert np.array_equal(got[d], first[d]), f"publishing order dest {d} differs"
     assert pub.ready_state() == (pub.ready_expected(), 0)
+
+
+def test_largest_group_full(gpu_lib):
+    """64 ranks of one head each (the most destinations a session takes), last
+    rank: every destination's slot against the oracle, other rows poisoned."""
+    wl = W.custom(21, batch=1, s_local=5, heads=64, world=64, rank=63, layout="fused",
+                  schedule=(1,), rope_base=1e4)
+    inp = Inputs(wl)
+    sess = make_session(gpu_lib, wl)
+    sess.poison_receive_slots()
+    views = run(sess, inp)
+    torch.cuda.synchronize()
+    check_full(views, inp, wl.rank, "u64")

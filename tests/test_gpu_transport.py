@@ -130,7 +130,8 @@ def test_merge_received_form(gpu_lib):
 
 
 @pytest.mark.parametrize("world,sched,fused", [(2, (7, 14, 7), True), (4, (2, 10, 2), False),
-                                               (8, (1, 4, 1), False), (1, (5, 3), True)])
+                                               (8, (1, 4, 1), False), (1, (5, 3), True),
+                                               (64, (1,), False)])
 def test_round_trip_all_ranks(gpu_lib, world, sched, fused):
     """Every rank packs every chunk into shared receive slots; merging each rank's
     rows back returns each rank's q, k and v bit for bit."""
