@@ -175,29 +175,42 @@ void fused_qkv_kernel(FusedArgs a) {
     const int wm = wave >> 1;     // which 128 tokens of the tile
 
     // ---- tile schedule ---------------------------------------------------------
-    // The logical tile order is split into queues: one per XCD (workgroups b
-    // with b % 8 == x run on XCD x and own a contiguous eighth of the order),
-    // or a single queue over the whole order with readiness words (so that
-    // destinations complete one after another) or a grid that is not a
-    // multiple of 8.  A queue's workgroups take its first two rounds (one tile
-    // each per round) in a fixed order; with tile-claim counters the rest is
-    // claimed one tile at a time (the workgroup's own queue first, then the
-    // others once it is used up), so that XCDs running at a higher clock take
-    // more tiles and all finish together.  Without counters the workgroups
-    // walk their queue a round at a time.
+    // The logical tile order is split into queues, one per XCD (workgroups b
+    // with b % 8 == x run on XCD x), or a single queue for a grid that is not
+    // a multiple of 8.  Queue x holds a contiguous share of the order; with
+    // readiness words the order is destination-major and is shared out one
+    // destination at a time (queue x: its share of destination 0's tiles,
+    // then of destination 1's, ...), so that destinations complete one after
+    // another while each XCD keeps runs of neighbouring tiles.  A queue's
+    // workgroups take its first two rounds (one tile each per round) in a
+    // fixed order; with tile-claim counters the rest is claimed one tile at a
+    // time (the workgroup's own queue first, then the others once it is used
+    // up), so that XCDs running at a higher clock take more tiles and all
+    // finish together.  Without counters the workgroups walk their queue a
+    // round at a time.
     const int G = gridDim.x;
     const int bid = blockIdx.x;
     const int total = a.tiles_m * a.tiles_n;
-    const bool by_xcd = G % NXCD == 0 && !a.ready;
+    const bool by_xcd = G % NXCD == 0;
     const int nq = by_xcd ? NXCD : 1;
     const bool claim = a.sched != nullptr;
-    const int per = total / nq, rem = total % nq;
-    auto range_start = [&](int x) { return x * per + min(x, rem); };
-    auto range_len = [&](int x) { return per + (x < rem ? 1 : 0); };
+    // span: the tiles shared out among the queues at a time (one destination's
+    // tiles, world of them in all, or the whole order)
+    const int span = a.ready && a.dest_cols > 0 ? a.tiles_m * 3 * a.dest_cols : total;
+    const int nspan = total / span;
+    const int per = span / nq, rem = span % nq;
+    auto share_start = [&](int x) { return x * per + min(x, rem); };
+    auto share_len = [&](int x) { return per + (x < rem ? 1 : 0); };
+    auto qlen = [&](int x) { return nspan * share_len(x); };
+    // logical tile at position i < qlen(x) of queue x
+    auto qtile = [&](int x, int i) {
+        const int len = share_len(x);
+        const int sp = i / len;
+        return sp * span + share_start(x) + (i - sp * len);
+    };
     const int xcd = by_xcd ? bid % NXCD : 0;        // the workgroup's queue
     const int stride = by_xcd ? G / NXCD : G;       // workgroups per queue
-    const int first = range_start(xcd) + (by_xcd ? bid / NXCD : bid);
-    const int end = range_start(xcd) + range_len(xcd);
+    const int qfirst = by_xcd ? bid / NXCD : bid;   // its first position in the queue
     // Once a workgroup has claimed its last tile it counts itself finished;
     // the last one to do so zeroes the counters for the next launch (every
     // claim of this launch has returned by then).
@@ -211,10 +224,11 @@ void fused_qkv_kernel(FusedArgs a) {
             }
         }
     };
-    if (first >= end) {
+    if (qfirst >= qlen(xcd)) {
         finish();
         return;
     }
+    const int first = qtile(xcd, qfirst);
     const int K = a.K;
     // With readiness words the order is destination-major: the tiles holding
     // destination d's heads (dest_cols columns in each of q, k, v) come before
@@ -306,7 +320,8 @@ void fused_qkv_kernel(FusedArgs a) {
     // nxt: the tile after the current one, or -1.
     int m0, n0, m0_next, n0_next, own, own_next;
     tile_origin(first, m0, n0, own);
-    int nxt = first + stride < end ? first + stride : -1;
+    int qnxt = qfirst + stride;                      // queue position of nxt (fixed order)
+    int nxt = qnxt < qlen(xcd) ? qtile(xcd, qnxt) : -1;
     tile_origin(nxt >= 0 ? nxt : first, m0_next, n0_next, own_next);
     uint32_t gw_cur = panel_offset(n0), gx_cur = panel_offset(m0);
     uint32_t gw_nxt = panel_offset(n0_next), gx_nxt = panel_offset(m0_next);
@@ -659,8 +674,8 @@ void fused_qkv_kernel(FusedArgs a) {
                 int t = -1;
                 for (;;) {
                     const int idx = 2 * stride + int(reply);
-                    if (idx < range_len(cvict)) {
-                        t = range_start(cvict) + idx;
+                    if (idx < qlen(cvict)) {
+                        t = qtile(cvict, idx);
                         break;
                     }
                     if (++ctried == nq) break;
@@ -676,7 +691,8 @@ void fused_qkv_kernel(FusedArgs a) {
                          : "=v"(got) : "v"(mail) : "memory");
             after = __builtin_amdgcn_readfirstlane(got);
         } else {
-            after = nxt + stride < end ? nxt + stride : -1;
+            qnxt += stride;
+            after = qnxt < qlen(xcd) ? qtile(xcd, qnxt) : -1;
         }
         m0 = m0_next;
         n0 = n0_next;
