@@ -207,6 +207,8 @@ def good_pack_args():
     (lambda a: setattr(a["dst"], "world", 4), -1),
     (lambda a: a["dst"].base.__setitem__(1, SRC[1] + 4096 - 64 * 1536 * 2), -5),  # rows land in k
     (lambda a: a["dst"].base.__setitem__(0, 0), -1),
+    (lambda a: a["q"].shape.__setitem__(1, 0), -1),         # empty: no tokens
+    (lambda a: [t.shape.__setitem__(0, 0) for t in (a["q"], a["k"], a["v"])], -1),  # no batch
 ])
 def test_pack_rejects(lib, mutate, status):
     q, k, v, dst = good_pack_args()
@@ -238,6 +240,8 @@ def merge(lib, src, world, local_heads, sched, chunk, out, batch, s_local):
     (dict(local_heads=0), -1),
     (dict(s_local=1000), -3),                  # source rows too few
     (dict(out=DST[0]), -5),
+    (dict(s_local=0), -1),                     # empty: no tokens
+    (dict(batch=0), -1),
 ])
 def test_merge_rejects(lib, kw, status):
     args = dict(world=2, local_heads=14, sched=[2, 10, 2], chunk=1, out=FAKE + (9 << 30),
@@ -274,6 +278,8 @@ def band_call(lib, name, x, world, dst):
     (lambda a: a["dst"].base.__setitem__(1, SRC[0] + 4096), -5),   # lands inside x
     (lambda a: a["dst"].base.__setitem__(0, 0), -1),
     (lambda a: a["dst"].base.__setitem__(0, DST[0] + 8), -4),
+    (lambda a: a["x"].shape.__setitem__(1, 0), -1),          # empty: no rows
+    (lambda a: a["x"].shape.__setitem__(2, 0), -1),          # empty: no heads
 ])
 def test_band_transforms_reject(lib, name, mutate, status):
     x = view(SRC[0], BAND_SHAPE, contiguous(BAND_SHAPE))
