@@ -240,15 +240,22 @@ int qkvx_create(int hidden, int num_heads, int head_dim, int world, int layout, 
 
 int qkvx_destroy(qkvx_session* s) {
     if (!s) return fail(QKVX_ERR_INVALID, "session is NULL");
-    if (s->ready) hipFree(s->ready);
-    if (s->sched) hipFree(s->sched);
-    if (s->owns_slots) {
-        hipError_t e = hipFree(s->slots);
-        delete s;
-        if (e != hipSuccess) return hip_fail(e, "hipFree of the receive slots");
-        return ok();
-    }
+    // every allocation is released; the first failure is reported
+    hipError_t first = hipSuccess;
+    const char* what = nullptr;
+    auto release = [&](void* p, const char* name) {
+        if (!p) return;
+        hipError_t e = hipFree(p);
+        if (e != hipSuccess && first == hipSuccess) {
+            first = e;
+            what = name;
+        }
+    };
+    release(s->ready, "hipFree of the readiness words");
+    release(s->sched, "hipFree of the tile-claim counters");
+    if (s->owns_slots) release(s->slots, "hipFree of the receive slots");
     delete s;
+    if (first != hipSuccess) return hip_fail(first, what);
     return ok();
 }
 
@@ -353,7 +360,7 @@ int qkvx_forward(qkvx_session* s, const void* x, int batch, int s_local, const v
             if (e == hipSuccess) e = hipMemset(mem, 0, kSchedWords * sizeof(unsigned int));
             if (e == hipSuccess) e = hipDeviceSynchronize();
             if (e != hipSuccess) {
-                if (mem) hipFree(mem);
+                if (mem) (void)hipFree(mem);   // the allocation error is the one reported
                 return hip_fail(e, "allocation of the tile-claim counters");
             }
             s->sched = static_cast<unsigned int*>(mem);
@@ -434,7 +441,7 @@ int qkvx_set_publish(qkvx_session* s, int enable) {
         hipError_t e = hipMalloc(&mem, bytes);
         if (e == hipSuccess) e = hipMemset(mem, 0, bytes);
         if (e != hipSuccess) {
-            if (mem) hipFree(mem);
+            if (mem) (void)hipFree(mem);   // the allocation error is the one reported
             return hip_fail(e, "allocation of the readiness words");
         }
         s->ready = static_cast<unsigned long long*>(mem);
