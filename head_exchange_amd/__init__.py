@@ -145,6 +145,21 @@ def _ptr(t) -> Optional[int]:
     return None if t is None else t.data_ptr()
 
 
+def _on_gpu(t, name):
+    """The library's kernels address device memory only: a host tensor's pointer
+    would fault on the GPU, so it is rejected here."""
+    if not getattr(t, "is_cuda", False):
+        raise ValueError(f"{name} must be a GPU tensor")
+
+
+def _check_f32(t, name, min_numel):
+    import torch
+    _on_gpu(t, name)
+    if t.dtype != torch.float32 or not t.is_contiguous() or t.numel() < min_numel:
+        raise ValueError(f"{name} must be a contiguous float32 tensor of at least "
+                         f"{min_numel} elements")
+
+
 def _check_bf16(t, name):
     import torch
     if t.dtype not in (torch.bfloat16, torch.int16, torch.uint16):
@@ -154,6 +169,7 @@ def _check_bf16(t, name):
 def view4(t) -> View4:
     """A [B, S, H, 128] tensor (any strides) as a qkvx_view4."""
     _check_bf16(t, "view")
+    _on_gpu(t, "view")
     if t.dim() != 4:
         raise ValueError("expected a 4-D tensor")
     v = View4()
@@ -176,6 +192,7 @@ def peers(tensors: Sequence, row_offset: int = 0, head_offset: int = 0) -> Peers
     p.head_offset = head_offset
     for u, t in enumerate(tensors):
         _check_bf16(t, f"peer {u}")
+        _on_gpu(t, f"peer {u}")
         if tuple(t.shape) != tuple(t0.shape) or t.stride() != t0.stride():
             raise ValueError("peer tensors must share shape and strides")
         if t.stride(3) != 1:
@@ -248,10 +265,15 @@ class Session:
         ``[(q, k, v), ...]`` for bshd, ``[payload, ...]`` for fused."""
         _check_bf16(x, "x")
         _check_bf16(w_qkv, "w_qkv")
+        _on_gpu(x, "x")
+        _on_gpu(w_qkv, "w_qkv")
         if x.dim() != 3 or not x.is_contiguous() or not w_qkv.is_contiguous():
             raise ValueError("x must be a contiguous [B, S_local, hidden] tensor and w_qkv contiguous")
-        if not cos_sin.is_contiguous():
-            raise ValueError("cos_sin must be contiguous")
+        _check_f32(q_norm_w, "q_norm_w", 128)
+        _check_f32(k_norm_w, "k_norm_w", 128)
+        _check_f32(cos_sin, "cos_sin", 0)
+        if cos_sin.dim() != 2 or cos_sin.shape[1] != 128:
+            raise ValueError("cos_sin must be a [rows, 128] float32 table")
         o = Outputs()
         _check(load().qkvx_forward(self._h, x.data_ptr(), x.shape[0], x.shape[1],
                                    w_qkv.data_ptr(), q_norm_w.data_ptr(), k_norm_w.data_ptr(),
@@ -351,6 +373,7 @@ def ulysses_merge_output_head_chunk(src: Sequence, *, world: int, local_heads: i
     ([B, rows, heads, 128]; rows ``row_offset..``, heads ``head_offset..``) into
     ``out`` ([B, S, world*local_heads, 128], contiguous)."""
     _check_bf16(out, "out")
+    _on_gpu(out, "out")
     if out.dim() != 4 or not out.is_contiguous():
         raise ValueError("out must be a contiguous [B, S_local, H, 128] tensor")
     sched, n = _schedule(schedule)
@@ -398,10 +421,12 @@ def ulysses_pack_output_sequence_chunk(x, *, world: int, dst: Sequence, row_offs
 def ulysses_exchange_chunks(x, *, world: int, rank: int, dst: Sequence, stream=None) -> None:
     """x: contiguous [..., world, chunk] tensor of any dtype; chunk u goes to
     ``dst[u]`` (same shape and dtype) at slot ``rank``."""
+    _on_gpu(x, "x")
     if not x.is_contiguous() or x.shape[-2] != world:
         raise ValueError("x must be a contiguous [..., world, chunk] tensor")
     chunk_bytes = x.numel() * x.element_size() // world
     for t in dst:
+        _on_gpu(t, "dst")
         if t.dtype != x.dtype or tuple(t.shape) != tuple(x.shape) or not t.is_contiguous():
             raise ValueError("every destination must be contiguous with x's shape and dtype")
     if len(dst) != world:
@@ -415,5 +440,7 @@ def qkvx_wait_word(word, expected: int, timeouts, *, spin_limit: int = 1 << 22,
                    stream=None) -> None:
     """Enqueue the wait kernel on a device uint64 ``word`` (a one-element int64
     tensor); a timeout adds 1 to the device int32 ``timeouts`` tensor."""
+    _on_gpu(word, "word")
+    _on_gpu(timeouts, "timeouts")
     _check(load().qkvx_wait_word(word.data_ptr(), int(expected), spin_limit, timeouts.data_ptr(),
                                  _stream(stream)))

@@ -350,3 +350,21 @@ def test_python_binding_fails_loudly_without_library(tmp_path):
             mod.load(str(tmp_path / "missing.so"))
     finally:
         mod._lib = saved
+
+
+def test_binding_rejects_host_tensors_before_any_call():
+    """The kernels address device memory only; the binding refuses host tensors
+    (their pointers would fault on the GPU) before the library is called."""
+    import torch
+    cpu = torch.zeros(1, 4, 2, 128, dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="GPU tensor"):
+        hx.view4(cpu)
+    with pytest.raises(ValueError, match="GPU tensor"):
+        hx.peers([cpu, cpu])
+    with pytest.raises(ValueError, match="GPU tensor"):
+        hx.ulysses_merge_output_head_chunk([cpu, cpu], world=2, local_heads=1, schedule=[1],
+                                           chunk=0, out=torch.zeros(1, 4, 2, 128,
+                                                                    dtype=torch.bfloat16))
+    with pytest.raises(ValueError, match="GPU tensor"):
+        hx.ulysses_exchange_chunks(torch.zeros(2, 16, dtype=torch.uint8), world=2, rank=0,
+                                   dst=[torch.zeros(2, 16, dtype=torch.uint8)] * 2)
