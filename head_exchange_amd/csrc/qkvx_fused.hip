@@ -100,8 +100,14 @@ __device__ __forceinline__ void tile_coords(int l, int tiles_m, int tiles_n, int
     tn = r / gsize;
 }
 
-__device__ __forceinline__ uint16_t bf16_bits(float f) {
-    return __builtin_bit_cast(uint16_t, static_cast<__bf16>(f));
+// Two floats rounded to bf16 (nearest even) and packed, lo in bits 0-15: one
+// v_cvt_pk_bf16_f32.  (Converting each float alone and packing the halves
+// costs three instructions per pair.)
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t bf16_pair(float lo, float hi) {
+    const f32x2 v = {lo, hi};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
 }
 
 // Accumulators are read with explicit v_accvgpr_read so that the compiler
@@ -482,12 +488,10 @@ void fused_qkv_kernel(FusedArgs a) {
 #pragma unroll
         for (int hh = 0; hh < 2; ++hh) {
             uint4 pk;
-            pk.x = uint32_t(bf16_bits(v[2 * hh][0])) | (uint32_t(bf16_bits(v[2 * hh][1])) << 16);
-            pk.y = uint32_t(bf16_bits(v[2 * hh][2])) | (uint32_t(bf16_bits(v[2 * hh][3])) << 16);
-            pk.z = uint32_t(bf16_bits(v[2 * hh + 1][0])) |
-                   (uint32_t(bf16_bits(v[2 * hh + 1][1])) << 16);
-            pk.w = uint32_t(bf16_bits(v[2 * hh + 1][2])) |
-                   (uint32_t(bf16_bits(v[2 * hh + 1][3])) << 16);
+            pk.x = bf16_pair(v[2 * hh][0], v[2 * hh][1]);
+            pk.y = bf16_pair(v[2 * hh][2], v[2 * hh][3]);
+            pk.z = bf16_pair(v[2 * hh + 1][0], v[2 * hh + 1][1]);
+            pk.w = bf16_pair(v[2 * hh + 1][2], v[2 * hh + 1][3]);
             out2[hh] = pk;
         }
     };
