@@ -429,6 +429,40 @@ void fused_qkv_kernel(FusedArgs a) {
     // next block's first loads.  Vector memory operations retire in order, so
     // a wait for loads also waits for every older store: stores are therefore
     // grouped (one group per m-block) and made of whole 64-byte runs.
+    // Per (m-block, q) a Q/K wave needs 4 weight vectors and 2 + 2 cos/sin
+    // vectors; they are loaded one q ahead into the other of two buffers.
+    //   Wq[i] = w[64 (i / 2) + 32 hf + 8 q + 4 (i % 2)]          (i < 4)
+    //   rotate-half: Cq[lo] = cs[row][32 hf + 8 q + 4 lo], Sq at + 64
+    //   interleaved: Cq[hi] = cs[row][32 hi + 16 hf + 4 q],  Sq at + 64
+    f32x4 Wb[2][4], Cb[2][2], Sb[2][2];
+    auto load_tables = [&](const float* nw, int row, int q, int buf) {
+        const float* csr = a.cs + int64_t(row) * 128;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            Wb[buf][i] = *reinterpret_cast<const f32x4*>(nw + 64 * (i >> 1) + 32 * hf + 8 * q +
+                                                         4 * (i & 1));
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const int off = ROPE_IL ? 32 * i + 16 * hf + 4 * q : 32 * hf + 8 * q + 4 * i;
+            Cb[buf][i] = *reinterpret_cast<const f32x4*>(csr + off);
+            Sb[buf][i] = *reinterpret_cast<const f32x4*>(csr + 64 + off);
+        }
+    };
+    // The first (m-block 0, q 0) values of a Q/K wave's tile, issued before
+    // the tile's last K-step: that step's end-of-step wait then covers them,
+    // instead of the epilogue waiting for them behind the ring loads of the
+    // next tile (vector memory operations retire in order).
+    auto first_tables = [&](int m0, int n0) {
+        const int ncol = n0 + wn * 128;
+        if (ncol >= a.N) return;
+        const int p = ncol / a.hidden;
+        if (p == 2) return;
+        const int m_tile = m0 + wm * 128 + mfma_row(0, fr);
+        const int m = m_tile < a.M ? m_tile : a.M - 1;
+        const int s = m - (m / a.s_local) * a.s_local;
+        load_tables(p == 0 ? a.wq : a.wk, a.row0 + s, 0, 0);
+    };
+
     auto epilogue = [&](int m0, int n0) {
     const int ncol = n0 + wn * 128;
     if (ncol >= a.N) return;
@@ -519,13 +553,8 @@ void fused_qkv_kernel(FusedArgs a) {
         return;
     }
 
-    // Per (m-block, q) the lane needs 4 weight vectors and 2 + 2 cos/sin
-    // vectors; they are loaded one q ahead into the other of two buffers.
-    //   Wq[i] = w[64 (i / 2) + 32 hf + 8 q + 4 (i % 2)]          (i < 4)
-    //   rotate-half: Cq[lo] = cs[row][32 hf + 8 q + 4 lo], Sq at + 64
-    //   interleaved: Cq[hi] = cs[row][32 hi + 16 hf + 4 q],  Sq at + 64
+    // m-block 0, q 0 of the tables are already loaded (first_tables)
     const float* nw = p == 0 ? a.wq : a.wk;
-    f32x4 Wb[2][4], Cb[2][2], Sb[2][2];
     int rows[4];
     bool in_range[4];
 #pragma unroll
@@ -533,20 +562,7 @@ void fused_qkv_kernel(FusedArgs a) {
         const auto br = token_row(mb, in_range[mb]);
         rows[mb] = br.y;
     }
-    auto load_q = [&](int mb, int q, int buf) {
-        const float* csr = a.cs + int64_t(rows[mb]) * 128;
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-            Wb[buf][i] = *reinterpret_cast<const f32x4*>(nw + 64 * (i >> 1) + 32 * hf + 8 * q +
-                                                         4 * (i & 1));
-#pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            const int off = ROPE_IL ? 32 * i + 16 * hf + 4 * q : 32 * hf + 8 * q + 4 * i;
-            Cb[buf][i] = *reinterpret_cast<const f32x4*>(csr + off);
-            Sb[buf][i] = *reinterpret_cast<const f32x4*>(csr + 64 + off);
-        }
-    };
-    load_q(0, 0, 0);
+    auto load_q = [&](int mb, int q, int buf) { load_tables(nw, rows[mb], q, buf); };
 
 #pragma unroll
     for (int mb = 0; mb < 4; ++mb) {
@@ -630,7 +646,9 @@ void fused_qkv_kernel(FusedArgs a) {
     asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(HLOADS) : "memory");
     for (;;) {
         step(0, true);
-        for (int kt = 1; kt < KT; ++kt) step(kt, false);
+        for (int kt = 1; kt < KT - 1; ++kt) step(kt, false);
+        first_tables(m0, n0);
+        step(KT - 1, false);
         // sub-step 3 of the last K-step (its fragments arrived before the barrier)
 #pragma unroll
         for (int nb = 0; nb < 4; ++nb)
