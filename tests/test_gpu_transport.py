@@ -183,3 +183,79 @@ def test_pack_rejects_bad_calls_without_writing(gpu_lib):
     torch.cuda.synchronize()
     for t in dst:
         assert bool((t.view(torch.int16) == POISON).all())
+
+
+def _random_bits(shape, seed):
+    """Seeded random 16-bit patterns drawn on the device in slices (these tensors
+    are too large to draw and upload from the host); the kernels under test only
+    copy bits, so every pattern serves, NaN patterns included."""
+    t = torch.empty(shape, dtype=torch.int16, device="cuda")
+    g = torch.Generator(device="cuda")
+    g.manual_seed(seed)
+    flat = t.view(-1)
+    step = 1 << 27
+    for i in range(0, flat.numel(), step):
+        n = min(step, flat.numel() - i)
+        flat[i:i + n] = torch.randint(-32768, 32767, (n,), generator=g, device="cuda",
+                                      dtype=torch.int16)
+    return t.view(torch.bfloat16)
+
+
+def _rows(t, idx):
+    """Rows idx of a [1, rows, ...] device tensor, as host bit patterns."""
+    return to_bits(t[0, torch.as_tensor(idx, device="cuda")].contiguous())
+
+
+def test_merge_and_pack_at_the_int32_limit(gpu_lib):
+    """Element offsets up to just under 2^31 (byte offsets past 2^32): a merge whose
+    band source and output each hold just under 2^31 elements, and a pack of
+    positive-stride q, k, v views of one [1, S, 56, 384] tensor of just under 2^31
+    elements into four receive slots at rank 3's rows.  Sampled tokens (both ends
+    and random ones) are compared bit for bit with the oracle's index maps; the
+    output starts poisoned, and heads and rows outside what was written keep it."""
+    U, hl, sched = 4, 14, (2, 10, 2)
+    H = U * hl
+    pairs = W.schedule_pairs(sched)
+    rng = np.random.default_rng(20261202)
+
+    # merge: band [1, U*S, hl, 128] -> out [1, S, H, 128], chunks 1 and 2
+    S = (2 ** 31 - 1) // (H * 128)
+    band = _random_bits((1, U * S, hl, 128), 7001)
+    out = poison_dev((1, S, H, 128))
+    srcs = [band[:, u * S:(u + 1) * S] for u in range(U)]
+    for chunk in (1, 2):
+        gpu_lib.ulysses_merge_output_head_chunk(srcs, world=U, local_heads=hl, schedule=sched,
+                                                chunk=chunk, out=out, head_offset=pairs[chunk][0])
+    torch.cuda.synchronize()
+    toks = np.unique(np.concatenate([[0, 1, S - 2, S - 1], rng.integers(0, S, 60)]))
+    got = _rows(out, toks)                                     # [T, H, 128]
+    src_rows = [_rows(band, toks + u * S) for u in range(U)]   # [T, hl, 128] each
+    ref = np.full((1, len(toks), H, 128), O.POISON_BITS, np.uint16)
+    for chunk in (1, 2):
+        off, cnt = pairs[chunk]
+        O.merge_output_head_chunk([r[None] for r in src_rows], 0, off, U, hl, off, cnt, ref)
+    assert np.array_equal(got, ref[0]), "merge at the int32 limit"
+    del band, out, srcs
+    torch.cuda.empty_cache()
+
+    # pack: q, k, v are views of one [1, S2, H, 384] tensor; chunk 1 (10 heads)
+    S2 = (2 ** 31 - 1) // (H * 384)
+    base = _random_bits((1, S2, H, 384), 7002)
+    q, k, v = base[..., :128], base[..., 128:256], base[..., 256:]
+    off, cnt = pairs[1]
+    r0 = 3 * S2
+    dst = [poison_dev((1, U * S2, cnt, 384)) for _ in range(U)]
+    gpu_lib.ulysses_pack_qkv_head_chunk(q, k, v, world=U, schedule=sched, chunk=1, dst=dst,
+                                        row_offset=r0)
+    torch.cuda.synchronize()
+    toks = np.unique(np.concatenate([[0, 1, S2 - 2, S2 - 1], rng.integers(0, S2, 60)]))
+    rows = _rows(base, toks)[None]                             # [1, T, H, 384]
+    refs = [np.full((1, len(toks), cnt, 384), O.POISON_BITS, np.uint16) for _ in range(U)]
+    O.pack_qkv_head_chunk_into(rows[..., :128], rows[..., 128:256], rows[..., 256:], U, off, cnt,
+                               refs, 0)
+    below = rng.integers(0, r0, 16)
+    for d in range(U):
+        assert np.array_equal(_rows(dst[d], toks + r0), refs[d][0]), f"pack dest {d}"
+        assert np.all(_rows(dst[d], below) == O.POISON_BITS), f"pack dest {d}: rows below"
+    del base, q, k, v, dst
+    torch.cuda.empty_cache()
