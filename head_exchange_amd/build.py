@@ -1,6 +1,6 @@
 """Build the gfx950 shared library ``libqkvx.so`` in-tree with hipcc.
 
-Run ``python -m head_exchange_amd.build`` (or ``__graft_entry__.build()``).  The
+Run ``python -m head_exchange_amd.build``.  The
 library is written next to this file so that it travels with the source tree.
 """
 from __future__ import annotations
