@@ -10,14 +10,18 @@
 //
 // Design (gfx950):
 //  * The GEMM is computed transposed, C^T[n, m] = W[n, :] . X[m, :], with
-//    v_mfma_f32_32x32x16_bf16.  In the 32x32 accumulator layout a lane owns one
-//    column (here: one token) and 16 rows (here: head dims), and lanes l and
-//    l+32 share the token.  A wave's 128-row n-range is exactly one head, so
-//    the RMS reduction over the head is a register sum plus one exchange with
-//    lane l^32, and both RoPE pairings keep their partners in one lane: the
-//    whole epilogue is lane-local.
+//    v_mfma_f32_16x16x32_bf16.  Under the chip's power limit this form does
+//    13 % more work than v_mfma_f32_32x32x16_bf16 (it moves half the
+//    accumulator bytes per multiply-add).  In the 16x16 accumulator layout a
+//    lane owns one column (here: one token) and four rows (here: head dims) of
+//    a block, and the four lanes l + 16 g share the token.  A wave's 128-row
+//    n-range is exactly one head, so the RMS reduction over the head is a
+//    register sum plus two exchanges, and both RoPE pairings keep their
+//    partners in one lane; with the operand rows staged in a fixed
+//    permutation, each lane holds four 16-byte runs of its token's head
+//    vector and the four lanes of a token together 64-byte runs.
 //  * Block tile 256 tokens x 256 columns (two heads), K-step 64, four waves in a
-//    2 x 2 grid, each owning one head x 128 tokens: 16 accumulators of 32x32
+//    2 x 2 grid, each owning one head x 128 tokens: 64 accumulators of 16x16
 //    per wave, all 256 AGPRs of the lane.
 //  * Operands are K-contiguous and go straight from global memory to LDS
 //    (buffer_load ... lds, bounds-checked: rows past M or N read as zero),
@@ -28,12 +32,12 @@
 //    the X half of one K-step: while the MFMAs use K-step k (two buffers), the
 //    X half of k+1 and the W half of k+2 load into the buffers K-step k-1 used,
 //    and the wait at the end of the step leaves the W half of k+2 in flight.
-//    Within a buffer the 16-byte chunks of each 8-row block are XOR-swizzled by
-//    the block index, so the fragment reads are free of bank conflicts.
-//  * The main loop is a fixed sequence per K-step: 64 MFMA slots in four
-//    phases (each phase one 16-deep sub-step of all 16 accumulators), the next
-//    sub-step's eight fragment reads right after the first eight MFMAs of a
-//    phase, and the 16 load instructions in the other half of the slots (a
+//    Within a buffer the 16-byte chunks of each row are XOR-swizzled by a
+//    function of the row, so the fragment reads are free of bank conflicts.
+//  * The main loop is a fixed sequence per K-step: 128 MFMA slots in two
+//    phases (each phase one 32-deep sub-step of all 64 accumulators), the next
+//    sub-step's fragment reads spread over the phase (a W block right after
+//    its last MFMA), and the 16 load instructions in slots without a read (a
 //    load holds the wave's issue for ~24 cycles).  MFMAs and
 //    fragment reads are written as inline assembly with explicit
 //    lgkmcnt waits: the buffer a read uses is only known at run time, and
@@ -49,9 +53,9 @@
 //    claim tiles one at a time from per-XCD counters (then from the other
 //    XCDs' ranges), and all XCDs finish together.
 //  * Epilogue: Q/K norm and RoPE in registers, with the weights and cos/sin
-//    values loaded one q ahead; stores are transposed within groups of four
-//    lanes so that each store instruction writes whole 64-byte runs, and go
-//    out once per m-block.
+//    values loaded one step ahead (the first before the tile's last K-step);
+//    each store instruction writes whole 64-byte runs, and an m-block's stores
+//    go out together.
 #include "qkvx_internal.h"
 
 namespace qkvx {
@@ -68,23 +72,25 @@ constexpr int BUF_CHUNKS = 2048;    // 16-byte chunks per buffer: 256 rows x 128
 constexpr int HLOADS = 8;      // load instructions per wave per half step
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
-// 16-byte chunk index, within one buffer, of chunk c (0..7) of tile row r:
-// block r / 8 holds rows 8 (r / 8) .. + 7, 128 bytes each, with chunk c of a
-// row at position c ^ (block % 8).  Fragment reads of one chunk by lanes whose
-// rows lie in eight consecutive blocks therefore hit eight different 16-byte
-// bank groups.
-__device__ __forceinline__ int lds_pos(int r, int c) {
-    const int b = r >> 3;
-    return b * 64 + (r & 7) * 8 + (c ^ (b & 7));
-}
+// LDS layout of one buffer: 256 rows of 128 bytes (eight 16-byte chunks); row
+// r sits at 16-byte position 8 r, with chunk c of the row at slot c ^ swz(r),
+//   swz(r) = 2 ((r / 8) % 4) + (r / 2) % 2.
+// The 16 lanes that read one chunk of a fragment at a time take rows
+// mfma_row(blk, 0..15): four 8-row blocks (r / 8 % 4 = 0..3) x rows 4 t + 0..3
+// of each, i.e. both row parities and both values of (r / 2) % 2, so the
+// (row parity, swizzled slot) pairs, which select the 16-byte bank group of a
+// read, are all different: the fragment reads are free of bank conflicts.
+__device__ __forceinline__ int lds_swz(int r) { return 2 * ((r >> 3) & 3) + ((r >> 1) & 1); }
 
-// Row of a wave's 128-row range that MFMA row i (0..31) of 32-row block blk
-// maps to.  Lanes i..i+7 read rows 8 apart, i.e. in eight consecutive blocks.
+// Row of a wave's 128-row range that row i (0..15) of 16-row MFMA block blk
+// (0..7) maps to: 32 (blk / 2) + 8 (i / 4) + 4 (blk % 2) + i % 4.  Accumulator
+// register r of lane group g (lanes 16 g .. 16 g + 15) holds block row
+// i = 4 g + r, so blocks 2h and 2h + 1 give lane group g the eight consecutive
+// rows 32 h + 8 g .. + 7, and block blk + 4 holds the rows 64 further on.
 __device__ __forceinline__ int mfma_row(int blk, int i) {
-    return 64 * (blk >> 1) + 8 * (i & 7) + 4 * (blk & 1) + (i >> 3);
+    return 32 * (blk >> 1) + 8 * (i >> 2) + 4 * (blk & 1) + (i & 3);
 }
 
 // Tile coordinates of logical tile l: groups of group_m tile rows, walked
@@ -116,44 +122,6 @@ __device__ __forceinline__ float acc_read(const float& a) {
     float v;
     asm volatile("v_accvgpr_read_b32 %0, %1" : "=v"(v) : "a"(a));
     return v;
-}
-
-// Lane exchange within groups of four lanes (DPP quad permutation).
-template <int CTRL>
-__device__ __forceinline__ uint32_t quad_perm(uint32_t v) {
-    return uint32_t(__builtin_amdgcn_mov_dpp(int(v), CTRL, 0xF, 0xF, false));
-}
-constexpr int kQuadSwap2 = 2 | 3 << 2 | 0 << 4 | 1 << 6;   // lane k reads lane k ^ 2
-constexpr int kQuadSwap1 = 1 | 0 << 2 | 3 << 4 | 2 << 6;   // lane k reads lane k ^ 1
-template <int I>
-constexpr int quad_bcast() { return I | I << 2 | I << 4 | I << 6; }   // every lane reads lane I
-
-// Transpose of 4 x 4 elements of 16 bytes within each group of four lanes:
-// on entry lane k holds pieces r[0..3] of its own row, on return r[i] holds
-// piece k of the row of lane i of the group.  Two exchange stages, between
-// lanes k and k ^ 2 (pieces with bit 1 set) and between k and k ^ 1 (bit 0).
-__device__ __forceinline__ void quad_transpose(uint4 (&r)[4], int k) {
-    const bool b1 = (k >> 1) & 1, b0 = k & 1;
-#pragma unroll
-    for (int jj = 0; jj < 2; ++jj) {
-        uint32_t* lo = reinterpret_cast<uint32_t*>(&r[jj]);
-        uint32_t* hi = reinterpret_cast<uint32_t*>(&r[jj + 2]);
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {
-            const uint32_t recv = quad_perm<kQuadSwap2>(b1 ? lo[c] : hi[c]);
-            if (b1) lo[c] = recv; else hi[c] = recv;
-        }
-    }
-#pragma unroll
-    for (int jj = 0; jj < 4; jj += 2) {
-        uint32_t* lo = reinterpret_cast<uint32_t*>(&r[jj]);
-        uint32_t* hi = reinterpret_cast<uint32_t*>(&r[jj + 1]);
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {
-            const uint32_t recv = quad_perm<kQuadSwap1>(b0 ? lo[c] : hi[c]);
-            if (b0) lo[c] = recv; else hi[c] = recv;
-        }
-    }
 }
 
 template <int N>
@@ -262,10 +230,10 @@ void fused_qkv_kernel(FusedArgs a) {
 
     // ---- global -> LDS: direct loads (buffer_load ... lds) ----------------------
     // Instruction i of wave w fills block b = 4 i + w of a half: lane L brings
-    // the chunk stored at position L % 8 of row L / 8 of the block, i.e. chunk
-    // (L % 8) ^ (b % 8) of panel row 8 b + L / 8; the eight lanes of a row fetch
-    // its whole 128-byte segment.  b % 8 = 4 (i % 2) + w, so even and odd
-    // instructions use two lane offsets that differ in bit 6.
+    // the chunk stored at slot L % 8 of row r = 8 b + L / 8 of the block, i.e.
+    // chunk (L % 8) ^ swz(r) of panel row r; the eight lanes of a row fetch its
+    // whole 128-byte segment.  swz(r) = 2 w + (L / 16) % 2 does not depend on
+    // the instruction, so every load of a lane uses the same chunk offset.
     const __amdgpu_buffer_rsrc_t rw = __builtin_amdgcn_make_buffer_rsrc(
         (void*)a.w, (short)0, int(uint32_t(a.N) * uint32_t(K) * 2u), 0x00020000);
     const __amdgpu_buffer_rsrc_t rx = __builtin_amdgcn_make_buffer_rsrc(
@@ -274,50 +242,62 @@ void fused_qkv_kernel(FusedArgs a) {
     const uint32_t rowbytes = uint32_t(K) * 2u;
     const int wv = wave;
     const uint32_t lrow = uint32_t(8 * wv + (lane >> 3));
-    const uint32_t lchunk = uint32_t((lane & 7) ^ wv) * 16u;
-    // this lane's byte offset of K-step 0 of a panel at row origin (even
-    // instructions; odd ones: ^ 64)
+    const uint32_t lchunk = uint32_t((lane & 7) ^ (2 * wv + ((lane >> 4) & 1))) * 16u;
+    // this lane's byte offset of K-step 0 of a panel at row origin
     auto panel_offset = [&](int origin) {
         return (uint32_t(origin) + lrow) * rowbytes + lchunk;
     };
 
-    // ---- fragment reads: lane i%32 owns MFMA row i%32 of each 32-row block ----
-    // Sub-step ks reads chunk 2 ks + hf of each row: the position of chunk hf
-    // with bits 1-2 flipped by 2 ks.  Byte offsets within a buffer:
-    const int fr = lane & 31;
-    const int hf = lane >> 5;
-    uint32_t wo[4][4], xo[4][4];                           // [ks][block]
+    // ---- fragment reads -------------------------------------------------------
+    // v_mfma_f32_16x16x32_bf16: lane L holds the A (W) and B (X) operand
+    // elements of block row (column) L % 16 and K 8 (L / 16) .. + 7, i.e. chunk
+    // 4 s + L / 16 of that row in sub-step s (0, 1) of a K-step; the result in
+    // register r of lane L is block row 4 (L / 16) + r of column L % 16.
+    // The byte offset of a fragment within a buffer is this lane's part for
+    // sub-step s plus a per-block constant, 4096 (blk / 2) + 512 (blk % 2),
+    // which rides in the read's immediate offset.
+    const int fi = lane & 15;          // block row read; result column (token)
+    const int fg = lane >> 4;          // K chunk read; result row group (head dims)
+    uint32_t wl[2], xl[2];
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks)
-#pragma unroll
-        for (int b = 0; b < 4; ++b) {
-            wo[ks][b] = uint32_t(lds_pos(wn * 128 + mfma_row(b, fr), hf) ^ (2 * ks)) * 16u;
-            xo[ks][b] = uint32_t(lds_pos(wm * 128 + mfma_row(b, fr), hf) ^ (2 * ks)) * 16u;
-        }
+    for (int sstep = 0; sstep < 2; ++sstep) {
+        const int c = 4 * sstep + fg;
+        const int rw_ = wn * 128 + mfma_row(0, fi), rx_ = wm * 128 + mfma_row(0, fi);
+        wl[sstep] = uint32_t((rw_ >> 3) * 64 + (rw_ & 7) * 8 + (c ^ lds_swz(rw_))) * 16u;
+        xl[sstep] = uint32_t((rx_ >> 3) * 64 + (rx_ & 7) * 8 + (c ^ lds_swz(rx_))) * 16u;
+    }
     typedef __attribute__((address_space(3))) uint4 lds_uint4;
     lds_uint4* ring3 = (lds_uint4*)ring;
     const uint32_t ring0 = uint32_t(reinterpret_cast<uintptr_t>(ring3));
 
-    f32x16 acc[4][4];
-    // fragments of one sub-step: four 32-row blocks of W (A operand) and of X
-    // (B operand); two sets, A and B
-    bf16x8 fa_a[4], fb_a[4], fa_b[4], fb_b[4];
+    f32x4 acc[8][8];
+    // fragments: the eight 16-row W blocks (A operand) of the sub-step being
+    // multiplied, each replaced by the next sub-step's block right after its
+    // last MFMA, and the eight X blocks (B operand) in two sets, the current
+    // sub-step's and the next one's
+    bf16x8 fa[8], fb[2][8];
 
     // One MFMA on accumulator (nb, mb); `init`: the tile's first product, with
     // a zero accumulator input (no separate zeroing).
-    auto mfma1 = [&](int nb, int mb, const bf16x8& fa, const bf16x8& fb, bool init) {
+    auto mfma1 = [&](int nb, int mb, const bf16x8& x_, const bf16x8& y_, bool init) __attribute__((always_inline)) {
         if (init)
-            asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0"
-                         : "=a"(acc[nb][mb]) : "v"(fa), "v"(fb));
+            asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, 0"
+                         : "=a"(acc[nb][mb]) : "v"(x_), "v"(y_));
         else
-            asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0"
-                         : "+a"(acc[nb][mb]) : "v"(fa), "v"(fb));
+            asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0"
+                         : "+a"(acc[nb][mb]) : "v"(x_), "v"(y_));
     };
-    // A fragment read.  Its result may only be used after a wait_lgkm that
-    // covers it: the compiler does not track it, and every use below is an
-    // MFMA placed after such a wait.
-    auto lds_read = [&](bf16x8& dst, uint32_t addr) {
-        asm volatile("ds_read_b128 %0, %1" : "=v"(dst) : "v"(addr));
+    // A fragment read of block blk.  Its result may only be used after a
+    // wait_lgkm that covers it: the compiler does not track it, and every use
+    // below is an MFMA placed after such a wait.
+    auto lds_read = [&](bf16x8& dst, uint32_t base, int blk) __attribute__((always_inline)) {
+        switch (blk) {
+#define QKVX_READ(B) case B: asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(dst) \
+                                          : "v"(base), "i"(4096 * ((B) >> 1) + 512 * ((B) & 1))); break;
+            QKVX_READ(0) QKVX_READ(1) QKVX_READ(2) QKVX_READ(3)
+            QKVX_READ(4) QKVX_READ(5) QKVX_READ(6) QKVX_READ(7)
+#undef QKVX_READ
+        }
     };
 
     const int KT = K / BK;
@@ -338,7 +318,6 @@ void fused_qkv_kernel(FusedArgs a) {
         const bool nx = kidx >= KT;
         const uint32_t g0 = is_w ? (nx ? gw_nxt : gw_cur) : (nx ? gx_nxt : gx_cur);
         const uint32_t kb = uint32_t(nx ? kidx - KT : kidx) * BK * 2u;
-        const uint32_t flip = (i & 1) ? 64u : 0u;
         const uint32_t roff = uint32_t(32 * i) * rowbytes;
         lds_uint4* dst = ring3 + buf * BUF_CHUNKS + (4 * i + wv) * 64;
         // The buffer's range check covers the VGPR offset but not the SGPR
@@ -346,7 +325,7 @@ void fused_qkv_kernel(FusedArgs a) {
         // the VGPR offset so that they read as zeros; otherwise every row read
         // exists and the instruction's row step rides in the SGPR offset with
         // the K offset, which keeps the loop free of address arithmetic.
-        const uint32_t voff = ROWS_CHECKED ? (g0 ^ flip) + roff : (g0 ^ flip);
+        const uint32_t voff = ROWS_CHECKED ? g0 + roff : g0;
         const uint32_t soff = ROWS_CHECKED ? kb : roff + kb;
         __builtin_amdgcn_raw_ptr_buffer_load_lds(is_w ? rw : rx,
                                                  (__attribute__((address_space(3))) void*)dst, 16,
@@ -354,110 +333,120 @@ void fused_qkv_kernel(FusedArgs a) {
     };
 
     // ---- main loop ------------------------------------------------------------
-    // K-step kt of the current tile, W half in buffer pw.  64 MFMA slots in
-    // four phases of 16 (phase 0: set B, the previous K-step's sub-step 3; 1:
-    // set A, sub-step 0; 2: set B, sub-step 1; 3: set A, sub-step 2).  After
-    // slot j < 8 of phase p comes fragment read j of sub-step p into the other
-    // set (that set's MFMAs all issued in the previous phase); after slots
-    // j = 8, 10, 12, 14 one of the 16 load instructions of the X half of
-    // K-step kt+1 and the W half of K-step kt+2, into the two buffers K-step
-    // kt-1 used.
+    // K-step kt of the current tile, W half in buffer pw: two phases of 64
+    // MFMA slots (16 cycles each), slot j = 8 nb + mb.  Phase 0 multiplies the
+    // previous K-step's sub-step 1 (its fragments are in registers) and reads
+    // sub-step 0 of K-step kt; phase 1 multiplies sub-step 0 and reads
+    // sub-step 1.  In a phase, X block k of the next sub-step is read after
+    // slot 8 k + 3 (into the other X set) and W block k after slot 8 k + 7, the
+    // last MFMA of the current W block k (block 7: after the phase).  The
+    // first row of MFMAs of a phase needs every X block and W block 0, i.e.
+    // all but the last read (wait lgkmcnt(1) before slot 0), and W block 7 is
+    // waited for before slot 8 (two reads issued since).  Loads go after slots
+    // 8 k + 5: in steady steps the X half of K-step kt+1 in phase 0 and the W
+    // half of K-step kt+2 in phase 1, into the two buffers K-step kt-1 used; in
+    // a tile's first step (phase 1 only) all 16, after slots 8 k + 1 and 8 k + 5.
     // The step ends waiting for all but the last eight loads (the W half of
     // kt+2, which stays in flight) and for the reads, then the barrier.  A
-    // tile's first step has no phase 0: its sub-step-0 fragments are read
-    // up front and phase 1 starts the accumulators.
+    // tile's first step has no phase 0: its sub-step-0 fragments are read up
+    // front and phase 1 starts the accumulators.
     int pw = 0;
-    auto step = [&](int kt, bool first_of_tile) {
+    auto step = [&](int kt, bool first_of_tile) __attribute__((always_inline)) {
         const int px = pw == 4 ? 0 : pw + 1;
         const int bx1 = pw >= 2 ? pw - 2 : pw + 3;       // (pw + 3) % 5
         const int bw2 = pw >= 1 ? pw - 1 : 4;            // (pw + 4) % 5
         const uint32_t wb = ring0 + uint32_t(pw) * (BUF_CHUNKS * 16);
         const uint32_t xb = ring0 + uint32_t(px) * (BUF_CHUNKS * 16);
-        const int i0 = first_of_tile ? 16 : 0;
+        // phase ph multiplies X set ph ^ 1 (phase 0: the previous K-step's
+        // sub-step 1, set 1; phase 1: sub-step 0, set 0) and reads sub-step ph
+        // into X set ph
+        auto phase = [&](const int ph, const bool init) __attribute__((always_inline)) {
+            const uint32_t wa = wb + wl[ph], xa = xb + xl[ph];
+#pragma unroll
+            for (int nb = 0; nb < 8; ++nb) {
+#pragma unroll
+                for (int mb = 0; mb < 8; ++mb) {
+                    if (nb == 0 && mb == 0) wait_lgkm<1>();
+                    if (nb == 1 && mb == 0) wait_lgkm<2>();
+                    mfma1(nb, mb, fa[nb], ph ? fb[0][mb] : fb[1][mb], init);
+                    if (mb == 3) lds_read(ph ? fb[1][nb] : fb[0][nb], xa, nb);
+                    if (mb == 7 && nb < 7) lds_read(fa[nb], wa, nb);
+                    if (mb == 5 || (init && mb == 1)) {
+                        const int v = init ? (nb * 2 + (mb == 5 ? 1 : 0)) : (ph * 8 + nb);
+                        if (v < HLOADS) load_one(false, v, kt + 1, bx1);
+                        else load_one(true, v - HLOADS, kt + 2, bw2);
+                    }
+                }
+            }
+            lds_read(fa[7], wa, 7);
+        };
         if (first_of_tile) {
 #pragma unroll
-            for (int b = 0; b < 4; ++b) lds_read(fa_a[b], wb + wo[0][b]);
-#pragma unroll
-            for (int b = 0; b < 4; ++b) lds_read(fb_a[b], xb + xo[0][b]);
-        }
-#pragma unroll
-        for (int i = 0; i < 64; ++i) {
-            if (i < i0) continue;
-            const int ph = i >> 4, j = i & 15;
-            const int nb = j >> 2, mb = j & 3;
-            // The first row (nb 0) of a phase needs read 4 + mb of the previous
-            // phase's eight, in order; the j reads issued in this phase so far
-            // come after them: at most 3 - mb + j = 3 may be outstanding.
-            if (ph > 0 && j < 4) wait_lgkm<3>();
-            if (ph & 1)
-                mfma1(nb, mb, fa_a[nb], fb_a[mb], first_of_tile && ph == 1);
-            else
-                mfma1(nb, mb, fa_b[nb], fb_b[mb], false);
-            // Loads go only into slots without a fragment read (j >= 8): a
-            // load instruction holds the wave's issue for ~24 cycles while it
-            // sends 64 addresses, which must fit beside the slot's MFMA.
-            // Steady steps use j = 8, 10, 12, 14 of every phase; a tile's
-            // first step every slot j >= 8 of phases 1 and 2.
-            const int v = first_of_tile ? ((ph - 1) * 8 + (j - 8)) : (ph * 4 + (j - 8) / 2);
-            if (j >= 8 && (first_of_tile ? ph <= 2 : (j & 1) == 0) && v < 2 * HLOADS) {
-                if (v < HLOADS) load_one(false, v, kt + 1, bx1);
-                else load_one(true, v - HLOADS, kt + 2, bw2);
+            for (int k = 0; k < 8; ++k) {
+                lds_read(fb[0][k], xb + xl[0], k);
+                lds_read(fa[k], wb + wl[0], k);
             }
-            if (j < 8) {
-                bf16x8* fa = (ph & 1) ? fa_b : fa_a;
-                bf16x8* fb = (ph & 1) ? fb_b : fb_a;
-                if (j < 4) lds_read(fa[j], wb + wo[ph][j]);
-                else lds_read(fb[j - 4], xb + xo[ph][j - 4]);
-            }
+            phase(1, true);
+        } else {
+            phase(0, false);
+            phase(1, false);
         }
         asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(HLOADS) : "memory");
         pw = pw >= 3 ? pw - 3 : pw + 2;                  // (pw + 2) % 5
     };
 
     // ---- epilogue: one head (128 columns) per wave ----------------------------
-    // Accumulator register reg of n-block nb in lane-half hf holds head dim
-    //   e = 64 (nb / 2) + 32 hf + 8 (reg % 4) + 4 (nb % 2) + reg / 4
-    // of the token of MFMA column fr of m-block mb, tile token
-    //   wm * 128 + mfma_row(mb, fr).
-    // Registers q, q+4, q+8, q+12 hold four consecutive dims; n-blocks 2h and
-    // 2h+1 continue each other (16 bytes of bf16); n-block nb+2 holds e + 64.
-    // Each m-block is read twice (sum of squares, then the outputs, four dims
-    // per n-block at a time), which keeps the VGPRs in use small.
+    // Accumulator register r of n-block nb in lane group fg holds head dim
+    //   e = 32 (nb / 2) + 8 fg + 4 (nb % 2) + r
+    // of the token of column fi of m-block mb, tile token
+    //   wm * 128 + mfma_row(mb, fi);
+    // so for each of H = 0..3 lane group fg holds the eight consecutive dims
+    // 32 H + 8 fg .. + 7 (16 bytes of bf16) in n-blocks 2H and 2H+1, n-block
+    // nb + 4 holds e + 64 (the rotate-half partner) and registers r, r ^ 1 the
+    // interleaved partners.  A token's 128 dims are spread over the four lanes
+    // fi + 16 fg, so the RMS reduction is a register sum plus two exchanges,
+    // and one store instruction writes, for each of 16 tokens, 64 contiguous
+    // bytes from four lanes: 16 requests of 64 bytes, no transposes.
+    // Each m-block is read twice (sum of squares, then the outputs), which
+    // keeps the VGPRs in use small.
     //
-    // Memory: the norm weights and cos/sin values of (m-block, q) are loaded
-    // while the previous q is computed; an m-block's stores go out after the
-    // next block's first loads.  Vector memory operations retire in order, so
-    // a wait for loads also waits for every older store: stores are therefore
-    // grouped (one group per m-block) and made of whole 64-byte runs.
-    // Per (m-block, q) a Q/K wave needs 4 weight vectors and 2 + 2 cos/sin
-    // vectors; they are loaded one q ahead into the other of two buffers.
-    //   Wq[i] = w[64 (i / 2) + 32 hf + 8 q + 4 (i % 2)]          (i < 4)
-    //   rotate-half: Cq[lo] = cs[row][32 hf + 8 q + 4 lo], Sq at + 64
-    //   interleaved: Cq[hi] = cs[row][32 hi + 16 hf + 4 q],  Sq at + 64
+    // Memory: the norm weights and cos/sin values of (m-block, half) are
+    // loaded while the previous half is computed; a Q/K m-block's stores go
+    // out after the next block's first loads.  Vector memory operations retire
+    // in order, so a wait for loads also waits for every older store: stores
+    // are therefore grouped (one group per m-block) and made of whole 64-byte
+    // runs.
+    // Step (mb, hp), hp = 0, 1, covers dims 32 hp + 8 fg + 0..7 (n-blocks
+    // 2 hp, 2 hp + 1) and their partners 64 further on (n-blocks 2 hp + 4,
+    // 2 hp + 5).  It needs 4 weight vectors and 2 + 2 cos/sin vectors:
+    //   W[2 u + c] = w[64 u + 32 hp + 8 fg + 4 c]                   (u, c < 2)
+    //   rotate-half: C[c] = cs[row][32 hp + 8 fg + 4 c],  S[c] at + 64
+    //   interleaved: C[u] = cs[row][16 (hp + 2 u) + 4 fg], S[u] at + 64
+    // loaded one step ahead into the other of two buffers.
     f32x4 Wb[2][4], Cb[2][2], Sb[2][2];
-    auto load_tables = [&](const float* nw, int row, int q, int buf) {
+    auto load_tables = [&](const float* nw, int row, int hp, int buf) {
         const float* csr = a.cs + int64_t(row) * 128;
 #pragma unroll
         for (int i = 0; i < 4; ++i)
-            Wb[buf][i] = *reinterpret_cast<const f32x4*>(nw + 64 * (i >> 1) + 32 * hf + 8 * q +
+            Wb[buf][i] = *reinterpret_cast<const f32x4*>(nw + 64 * (i >> 1) + 32 * hp + 8 * fg +
                                                          4 * (i & 1));
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
-            const int off = ROPE_IL ? 32 * i + 16 * hf + 4 * q : 32 * hf + 8 * q + 4 * i;
+            const int off = ROPE_IL ? 16 * (hp + 2 * i) + 4 * fg : 32 * hp + 8 * fg + 4 * i;
             Cb[buf][i] = *reinterpret_cast<const f32x4*>(csr + off);
             Sb[buf][i] = *reinterpret_cast<const f32x4*>(csr + 64 + off);
         }
     };
-    // The first (m-block 0, q 0) values of a Q/K wave's tile, issued before
-    // the tile's last K-step: that step's end-of-step wait then covers them,
-    // instead of the epilogue waiting for them behind the ring loads of the
-    // next tile (vector memory operations retire in order).
+    // The first step's (m-block 0, half 0) values of a Q/K wave's tile, issued
+    // before the tile's last K-step: that step's end-of-step wait then covers
+    // them, instead of the epilogue waiting for them behind the ring loads of
+    // the next tile (vector memory operations retire in order).
     auto first_tables = [&](int m0, int n0) {
         const int ncol = n0 + wn * 128;
         if (ncol >= a.N) return;
         const int p = ncol / a.hidden;
         if (p == 2) return;
-        const int m_tile = m0 + wm * 128 + mfma_row(0, fr);
+        const int m_tile = m0 + wm * 128 + mfma_row(0, fi);
         const int m = m_tile < a.M ? m_tile : a.M - 1;
         const int s = m - (m / a.s_local) * a.s_local;
         load_tables(p == 0 ? a.wq : a.wk, a.row0 + s, 0, 0);
@@ -475,77 +464,47 @@ void fused_qkv_kernel(FusedArgs a) {
     // token of m-block mb: tokens past M (ragged last tile) are computed on
     // token M - 1 and not stored
     auto token_row = [&](int mb, bool& in_range) {
-        const int m_tile = m0 + wm * 128 + mfma_row(mb, fr);
+        const int m_tile = m0 + wm * 128 + mfma_row(mb, fi);
         in_range = m_tile < a.M;
         const int m = in_range ? m_tile : a.M - 1;
         const int bidx = m / a.s_local;
         const int s = m - bidx * a.s_local;
         return make_int2(bidx, a.row0 + s);   // batch, sequence row == position
     };
-    // Stores of one m-block.  Lane (fr, hf) holds 16-byte pieces q = 0..3 of
-    // dims 64 hh + 32 hf + 8 q of its token; after a transpose within each
-    // group of four lanes (four tokens), store i of a group writes the four
-    // pieces of one token's 64 contiguous bytes, so that each store makes 16
-    // requests of 64 bytes instead of 64 of 16.
+    // Stores of one m-block: out[H] holds dims 32 H + 8 fg .. + 7 of this
+    // lane's token, at byte 64 H + 16 fg of its 256-byte head vector.
     auto store_block = [&](uint16_t* orow, bool in_range, const uint4* out) {
-        const int k = fr & 3;
-        uint4 r[2][4];
+        if (!in_range) return;
 #pragma unroll
-        for (int hh = 0; hh < 2; ++hh) {
-#pragma unroll
-            for (int q = 0; q < 4; ++q) r[hh][q] = out[2 * q + hh];
-            quad_transpose(r[hh], k);
-        }
-        // store i: the row of group lane i (its pointer and range flag read
-        // from that lane), this lane's piece k
-        const uint64_t rowp = reinterpret_cast<uint64_t>(orow);
-        const uint32_t rlo = uint32_t(rowp), rhi = uint32_t(rowp >> 32), ok = in_range;
-        const uint64_t off = uint64_t(64 * hf + 16 * k);          // bytes
-        auto put = [&](uint32_t lo, uint32_t hi, uint32_t f, int i) {
-            if (f) {
-                uint16_t* dst = reinterpret_cast<uint16_t*>(((uint64_t(hi) << 32) | lo) + off);
-#pragma unroll
-                for (int hh = 0; hh < 2; ++hh)
-                    *reinterpret_cast<uint4*>(dst + 64 * hh) = r[hh][i];
-            }
-        };
-        put(quad_perm<quad_bcast<0>()>(rlo), quad_perm<quad_bcast<0>()>(rhi),
-            quad_perm<quad_bcast<0>()>(ok), 0);
-        put(quad_perm<quad_bcast<1>()>(rlo), quad_perm<quad_bcast<1>()>(rhi),
-            quad_perm<quad_bcast<1>()>(ok), 1);
-        put(quad_perm<quad_bcast<2>()>(rlo), quad_perm<quad_bcast<2>()>(rhi),
-            quad_perm<quad_bcast<2>()>(ok), 2);
-        put(quad_perm<quad_bcast<3>()>(rlo), quad_perm<quad_bcast<3>()>(rhi),
-            quad_perm<quad_bcast<3>()>(ok), 3);
+        for (int H = 0; H < 4; ++H)
+            *reinterpret_cast<uint4*>(orow + 32 * H + 8 * fg) = out[H];
     };
-    auto pack = [&](const float (&v)[4][4], uint4* out2) {
-#pragma unroll
-        for (int hh = 0; hh < 2; ++hh) {
-            uint4 pk;
-            pk.x = bf16_pair(v[2 * hh][0], v[2 * hh][1]);
-            pk.y = bf16_pair(v[2 * hh][2], v[2 * hh][3]);
-            pk.z = bf16_pair(v[2 * hh + 1][0], v[2 * hh + 1][1]);
-            pk.w = bf16_pair(v[2 * hh + 1][2], v[2 * hh + 1][3]);
-            out2[hh] = pk;
-        }
+    // eight consecutive dims (n-blocks 2H and 2H+1) -> one 16-byte piece
+    auto pack8 = [&](const float (&v)[2][4]) {
+        uint4 pk;
+        pk.x = bf16_pair(v[0][0], v[0][1]);
+        pk.y = bf16_pair(v[0][2], v[0][3]);
+        pk.z = bf16_pair(v[1][0], v[1][1]);
+        pk.w = bf16_pair(v[1][2], v[1][3]);
+        return pk;
     };
 
     if (p == 2) {
         // V: rounding and placement only
 #pragma unroll
-        for (int mb = 0; mb < 4; ++mb) {
+        for (int mb = 0; mb < 8; ++mb) {
             bool in_range;
             const auto br = token_row(mb, in_range);
             uint16_t* orow = dbase + int64_t(br.x) * a.stride_b + int64_t(br.y) * a.stride_s;
-            uint4 out[8];
+            uint4 out[4];
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                float v[4][4];
+            for (int H = 0; H < 4; ++H) {
+                float v[2][4];
 #pragma unroll
-                for (int nb = 0; nb < 4; ++nb)
+                for (int t = 0; t < 2; ++t)
 #pragma unroll
-                    for (int g = 0; g < 4; ++g) v[nb][g] = acc_read(acc[nb][mb][q + 4 * g]);
-                pack(v, out + 2 * q);
+                    for (int r = 0; r < 4; ++r) v[t][r] = acc_read(acc[2 * H + t][mb][r]);
+                out[H] = pack8(v);
             }
             store_block(orow, in_range, out);
         }
@@ -553,74 +512,84 @@ void fused_qkv_kernel(FusedArgs a) {
         return;
     }
 
-    // m-block 0, q 0 of the tables are already loaded (first_tables)
+    // step 0 (m-block 0, half 0) of the tables is already loaded (first_tables)
     const float* nw = p == 0 ? a.wq : a.wk;
-    int rows[4];
-    bool in_range[4];
+    int rows[8];
+    bool in_range[8];
 #pragma unroll
-    for (int mb = 0; mb < 4; ++mb) {
+    for (int mb = 0; mb < 8; ++mb) {
         const auto br = token_row(mb, in_range[mb]);
         rows[mb] = br.y;
     }
-    auto load_q = [&](int mb, int q, int buf) { load_tables(nw, rows[mb], q, buf); };
+    auto load_step = [&](int mb, int hp, int buf) { load_tables(nw, rows[mb], hp, buf); };
 
 #pragma unroll
-    for (int mb = 0; mb < 4; ++mb) {
-        // RMSNorm over the head's 128 values: 64 here, 64 in lane ^ 32
+    for (int mb = 0; mb < 8; ++mb) {
+        // RMSNorm over the head's 128 values: 32 here, 96 in lanes ^ 16, ^ 32
         float ss = 0.f;
 #pragma unroll
-        for (int nb = 0; nb < 4; ++nb)
+        for (int nb = 0; nb < 8; ++nb)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
+            for (int r = 0; r < 4; ++r) {
                 const float t = acc_read(acc[nb][mb][r]);
                 ss += t * t;
             }
+        ss += __shfl_xor(ss, 16);
         ss += __shfl_xor(ss, 32);
         const float inv = rsqrtf(ss * (1.0f / 128.0f) + a.eps);
-        uint4 out[8];
+        uint4 out[4];
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const int cur = (4 * mb + q) & 1;
-            if (4 * mb + q < 15) load_q(q < 3 ? mb : mb + 1, (q + 1) & 3, cur ^ 1);
-            // v[nb][g] = dim e(nb, q) + g, g = 0..3 (registers q + 4 g)
-            float v[4][4];
+        for (int hp = 0; hp < 2; ++hp) {
+            const int cur = (2 * mb + hp) & 1;
+            if (2 * mb + hp < 15) load_step(hp == 0 ? mb : mb + 1, hp ^ 1, cur ^ 1);
+            // lo[t][r]: dim 32 hp + 8 fg + 4 t + r; hi: the same + 64
+            float lo[2][4], hi[2][4];
 #pragma unroll
-            for (int nb = 0; nb < 4; ++nb)
+            for (int t = 0; t < 2; ++t)
 #pragma unroll
-                for (int g = 0; g < 4; ++g) v[nb][g] = acc_read(acc[nb][mb][q + 4 * g]);
-            if (ROPE_IL) {
-                // pairs (2i, 2i+1) = dims (E, E+1) and (E+2, E+3) of each
-                // n-block, E = e(nb, q), rotated by the angles of table columns
-                // E/2 and E/2 + 1
-#pragma unroll
-                for (int nb = 0; nb < 4; ++nb) {
-                    const f32x4 wt = Wb[cur][nb];
-                    const f32x4 cv = Cb[cur][nb >> 1], sv = Sb[cur][nb >> 1];
-#pragma unroll
-                    for (int gp = 0; gp < 2; ++gp) {
-                        const float z0 = v[nb][2 * gp] * (inv * wt[2 * gp]);
-                        const float z1 = v[nb][2 * gp + 1] * (inv * wt[2 * gp + 1]);
-                        const float c = cv[2 * (nb & 1) + gp], sn = sv[2 * (nb & 1) + gp];
-                        v[nb][2 * gp] = z0 * c - z1 * sn;
-                        v[nb][2 * gp + 1] = z1 * c + z0 * sn;
-                    }
+                for (int r = 0; r < 4; ++r) {
+                    lo[t][r] = acc_read(acc[2 * hp + t][mb][r]);
+                    hi[t][r] = acc_read(acc[2 * hp + 4 + t][mb][r]);
                 }
+            if (ROPE_IL) {
+                // pairs (2i, 2i+1) = registers (r, r+1), r = 0, 2, of each
+                // n-block; run u (lo, hi) rotates by table columns
+                // 16 (hp + 2 u) + 4 fg + 2 t + r / 2
+                auto rotate_run = [&](float (&v)[2][4], const int u) __attribute__((always_inline)) {
+                    const f32x4 cv = Cb[cur][u], sv = Sb[cur][u];
+#pragma unroll
+                    for (int t = 0; t < 2; ++t) {
+                        const f32x4 wt = Wb[cur][2 * u + t];
+#pragma unroll
+                        for (int gp = 0; gp < 2; ++gp) {
+                            const float z0 = v[t][2 * gp] * (inv * wt[2 * gp]);
+                            const float z1 = v[t][2 * gp + 1] * (inv * wt[2 * gp + 1]);
+                            const float c = cv[2 * t + gp], sn = sv[2 * t + gp];
+                            v[t][2 * gp] = z0 * c - z1 * sn;
+                            v[t][2 * gp + 1] = z1 * c + z0 * sn;
+                        }
+                    }
+                };
+                rotate_run(lo, 0);
+                rotate_run(hi, 1);
             } else {
-                // rotate-half: n-blocks lo and lo + 2 hold dims e and e + 64
+                // rotate-half: lo and hi hold dims e and e + 64, angle column
+                // 32 hp + 8 fg + 4 t + r
 #pragma unroll
-                for (int lo = 0; lo < 2; ++lo) {
-                    const f32x4 wl = Wb[cur][lo], wh = Wb[cur][2 + lo];
-                    const f32x4 cv = Cb[cur][lo], sv = Sb[cur][lo];
+                for (int t = 0; t < 2; ++t) {
+                    const f32x4 wl_ = Wb[cur][t], wh_ = Wb[cur][2 + t];
+                    const f32x4 cv = Cb[cur][t], sv = Sb[cur][t];
 #pragma unroll
-                    for (int g = 0; g < 4; ++g) {
-                        const float zl = v[lo][g] * (inv * wl[g]);
-                        const float zh = v[lo + 2][g] * (inv * wh[g]);
-                        v[lo][g] = zl * cv[g] - zh * sv[g];
-                        v[lo + 2][g] = zh * cv[g] + zl * sv[g];
+                    for (int r = 0; r < 4; ++r) {
+                        const float zl = lo[t][r] * (inv * wl_[r]);
+                        const float zh = hi[t][r] * (inv * wh_[r]);
+                        lo[t][r] = zl * cv[r] - zh * sv[r];
+                        hi[t][r] = zh * cv[r] + zl * sv[r];
                     }
                 }
             }
-            pack(v, out + 2 * q);
+            out[hp] = pack8(lo);
+            out[hp + 2] = pack8(hi);
             __builtin_amdgcn_sched_barrier(0);
         }
         // this block's stores go out after the next block's first loads
@@ -649,11 +618,11 @@ void fused_qkv_kernel(FusedArgs a) {
         for (int kt = 1; kt < KT - 1; ++kt) step(kt, false);
         first_tables(m0, n0);
         step(KT - 1, false);
-        // sub-step 3 of the last K-step (its fragments arrived before the barrier)
+        // sub-step 1 of the last K-step (its fragments arrived before the barrier)
 #pragma unroll
-        for (int nb = 0; nb < 4; ++nb)
+        for (int nb = 0; nb < 8; ++nb)
 #pragma unroll
-            for (int mb = 0; mb < 4; ++mb) mfma1(nb, mb, fa_b[nb], fb_b[mb], false);
+            for (int mb = 0; mb < 8; ++mb) mfma1(nb, mb, fa[nb], fb[1][mb], false);
         // the nops give the last MFMAs' results the wait states an accumulator
         // read needs
         asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
