@@ -339,10 +339,10 @@ void fused_qkv_kernel(FusedArgs a) {
     // sub-step 0 of K-step kt; phase 1 multiplies sub-step 0 and reads
     // sub-step 1.  In a phase, X block k of the next sub-step is read after
     // slot 8 k + 3 (into the other X set) and W block k after slot 8 k + 7, the
-    // last MFMA of the current W block k (block 7: after the phase).  The
-    // first row of MFMAs of a phase needs every X block and W block 0, i.e.
-    // all but the last read (wait lgkmcnt(1) before slot 0), and W block 7 is
-    // waited for before slot 8 (two reads issued since).  Loads go after slots
+    // last MFMA of the current W block k (block 7: after the phase).  Slot mb
+    // of the first row of MFMAs of a phase waits for X block mb and W block 0
+    // of the previous phase's reads, and W block 7 is waited for before slot 8
+    // (two reads issued since).  Loads go after slots
     // 8 k + 5: in steady steps the X half of K-step kt+1 in phase 0 and the W
     // half of K-step kt+2 in phase 1, into the two buffers K-step kt-1 used; in
     // a tile's first step (phase 1 only) all 16, after slots 8 k + 1 and 8 k + 5.
@@ -366,7 +366,20 @@ void fused_qkv_kernel(FusedArgs a) {
             for (int nb = 0; nb < 8; ++nb) {
 #pragma unroll
                 for (int mb = 0; mb < 8; ++mb) {
-                    if (nb == 0 && mb == 0) wait_lgkm<1>();
+                    // row 0 waits for exactly the reads it uses: X block mb and
+                    // W block 0 of the previous phase (in read order X0, W0,
+                    // X1, W1, ..., X7, W7; this phase's X0 follows slot 3);
+                    // slot 8 waits for W block 7 (two reads issued since)
+                    if (nb == 0) {
+                        if (mb == 0) wait_lgkm<14>();
+                        if (mb == 1) wait_lgkm<13>();
+                        if (mb == 2) wait_lgkm<11>();
+                        if (mb == 3) wait_lgkm<9>();
+                        if (mb == 4) wait_lgkm<8>();
+                        if (mb == 5) wait_lgkm<6>();
+                        if (mb == 6) wait_lgkm<4>();
+                        if (mb == 7) wait_lgkm<2>();
+                    }
                     if (nb == 1 && mb == 0) wait_lgkm<2>();
                     mfma1(nb, mb, fa[nb], ph ? fb[0][mb] : fb[1][mb], init);
                     if (mb == 3) lds_read(ph ? fb[1][nb] : fb[0][nb], xa, nb);
