@@ -420,8 +420,8 @@ void fused_qkv_kernel(FusedArgs a) {
     // fi + 16 fg, so the RMS reduction is a register sum plus two exchanges,
     // and one store instruction writes, for each of 16 tokens, 64 contiguous
     // bytes from four lanes: 16 requests of 64 bytes, no transposes.
-    // Each m-block is read twice (sum of squares, then the outputs), which
-    // keeps the VGPRs in use small.
+    // Each m-block's 32 values per lane are read from the accumulators once,
+    // for the sum of squares, and kept in VGPRs for the outputs.
     //
     // Memory: the norm weights and cos/sin values of (m-block, half) are
     // loaded while the previous half is computed; a Q/K m-block's stores go
@@ -538,14 +538,16 @@ void fused_qkv_kernel(FusedArgs a) {
 
 #pragma unroll
     for (int mb = 0; mb < 8; ++mb) {
-        // RMSNorm over the head's 128 values: 32 here, 96 in lanes ^ 16, ^ 32
+        // RMSNorm over the head's 128 values: 32 here, 96 in lanes ^ 16, ^ 32;
+        // the block's 32 values are read from the accumulators once
+        float y[8][4];
         float ss = 0.f;
 #pragma unroll
         for (int nb = 0; nb < 8; ++nb)
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                const float t = acc_read(acc[nb][mb][r]);
-                ss += t * t;
+                y[nb][r] = acc_read(acc[nb][mb][r]);
+                ss += y[nb][r] * y[nb][r];
             }
         ss += __shfl_xor(ss, 16);
         ss += __shfl_xor(ss, 32);
@@ -561,8 +563,8 @@ void fused_qkv_kernel(FusedArgs a) {
             for (int t = 0; t < 2; ++t)
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
-                    lo[t][r] = acc_read(acc[2 * hp + t][mb][r]);
-                    hi[t][r] = acc_read(acc[2 * hp + 4 + t][mb][r]);
+                    lo[t][r] = y[2 * hp + t][r];
+                    hi[t][r] = y[2 * hp + 4 + t][r];
                 }
             if (ROPE_IL) {
                 // pairs (2i, 2i+1) = registers (r, r+1), r = 0, 2, of each
