@@ -407,7 +407,7 @@ int qkvx_describe(const qkvx_session* s, char* buf, size_t len) {
         "\"region_elems\": %lld, \"slot_bytes\": %zu, \"owns_slots\": %s, \"calls\": %lld, "
         "\"next_slot\": %d, \"rope\": \"%s\", \"publish\": %s, \"eps\": 1e-6, "
         "\"tile\": {\"block_m\": %d, \"block_n\": %d, \"block_k\": %d, \"threads\": %d, "
-        "\"group_m\": %d, \"mfma\": \"v_mfma_f32_32x32x16_bf16\", \"xcd_remap\": 8}}",
+        "\"group_m\": %d, \"mfma\": \"v_mfma_f32_16x16x32_bf16\", \"xcd_remap\": 8}}",
         s->hidden, s->heads, QKVX_HEAD_DIM, s->world, s->heads / s->world,
         s->layout == QKVX_LAYOUT_BSHD ? "bshd" : "fused", (long long)s->max_tokens,
         s->num_slots, (long long)s->region_elems, s->slot_bytes, s->owns_slots ? "true" : "false",
