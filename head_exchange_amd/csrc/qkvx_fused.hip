@@ -116,6 +116,19 @@ __device__ __forceinline__ uint32_t bf16_pair(float lo, float hi) {
     return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
 }
 
+// Sum of v over the four lanes l ^ 16 k (k = 0..3) that share l % 16: two
+// permlane swaps (lanes 16-31 <-> 0-15 and 48-63 <-> 32-47; then the two
+// 32-lane halves), each followed by an add of the pair, which is the same sum
+// in the same order as two xor-shuffle steps, without an LDS round trip.
+__device__ __forceinline__ float sum_lane_groups(float v) {
+    const unsigned int u = __float_as_uint(v);
+    const auto r16 = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+    const float s = __uint_as_float(r16[0]) + __uint_as_float(r16[1]);
+    const unsigned int w = __float_as_uint(s);
+    const auto r32 = __builtin_amdgcn_permlane32_swap(w, w, false, false);
+    return __uint_as_float(r32[0]) + __uint_as_float(r32[1]);
+}
+
 // Accumulators are read with explicit v_accvgpr_read so that the compiler
 // never copies all 256 of them into VGPRs at once (there is no room).
 __device__ __forceinline__ float acc_read(const float& a) {
@@ -549,8 +562,7 @@ void fused_qkv_kernel(FusedArgs a) {
                 y[nb][r] = acc_read(acc[nb][mb][r]);
                 ss += y[nb][r] * y[nb][r];
             }
-        ss += __shfl_xor(ss, 16);
-        ss += __shfl_xor(ss, 32);
+        ss = sum_lane_groups(ss);
         const float inv = rsqrtf(ss * (1.0f / 128.0f) + a.eps);
         uint4 out[4];
 #pragma unroll
