@@ -444,18 +444,23 @@ void fused_qkv_kernel(FusedArgs a) {
     // runs.
     // Step (mb, hp), hp = 0, 1, covers dims 32 hp + 8 fg + 0..7 (n-blocks
     // 2 hp, 2 hp + 1) and their partners 64 further on (n-blocks 2 hp + 4,
-    // 2 hp + 5).  It needs 4 weight vectors and 2 + 2 cos/sin vectors:
-    //   W[2 u + c] = w[64 u + 32 hp + 8 fg + 4 c]                   (u, c < 2)
+    // 2 hp + 5).  It needs 4 weight vectors, the same for every m-block (loaded
+    // once per tile for both halves), and 2 + 2 cos/sin vectors of its token,
+    // loaded one step ahead into the other of two buffers:
+    //   W[hp][2 u + c] = w[64 u + 32 hp + 8 fg + 4 c]               (u, c < 2)
     //   rotate-half: C[c] = cs[row][32 hp + 8 fg + 4 c],  S[c] at + 64
     //   interleaved: C[u] = cs[row][16 (hp + 2 u) + 4 fg], S[u] at + 64
-    // loaded one step ahead into the other of two buffers.
-    f32x4 Wb[2][4], Cb[2][2], Sb[2][2];
-    auto load_tables = [&](const float* nw, int row, int hp, int buf) {
-        const float* csr = a.cs + int64_t(row) * 128;
+    f32x4 Wf[2][4], Cb[2][2], Sb[2][2];
+    auto load_weights = [&](const float* nw) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-            Wb[buf][i] = *reinterpret_cast<const f32x4*>(nw + 64 * (i >> 1) + 32 * hp + 8 * fg +
-                                                         4 * (i & 1));
+        for (int hp = 0; hp < 2; ++hp)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                Wf[hp][i] = *reinterpret_cast<const f32x4*>(nw + 64 * (i >> 1) + 32 * hp +
+                                                            8 * fg + 4 * (i & 1));
+    };
+    auto load_tables = [&](int row, int hp, int buf) {
+        const float* csr = a.cs + int64_t(row) * 128;
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
             const int off = ROPE_IL ? 16 * (hp + 2 * i) + 4 * fg : 32 * hp + 8 * fg + 4 * i;
@@ -475,7 +480,8 @@ void fused_qkv_kernel(FusedArgs a) {
         const int m_tile = m0 + wm * 128 + mfma_row(0, fi);
         const int m = m_tile < a.M ? m_tile : a.M - 1;
         const int s = m - (m / a.s_local) * a.s_local;
-        load_tables(p == 0 ? a.wq : a.wk, a.row0 + s, 0, 0);
+        load_weights(p == 0 ? a.wq : a.wk);
+        load_tables(a.row0 + s, 0, 0);
     };
 
     auto epilogue = [&](int m0, int n0) {
@@ -538,8 +544,8 @@ void fused_qkv_kernel(FusedArgs a) {
         return;
     }
 
-    // step 0 (m-block 0, half 0) of the tables is already loaded (first_tables)
-    const float* nw = p == 0 ? a.wq : a.wk;
+    // the weights and step 0 (m-block 0, half 0) of the table are already
+    // loaded (first_tables)
     int rows[8];
     bool in_range[8];
 #pragma unroll
@@ -547,7 +553,7 @@ void fused_qkv_kernel(FusedArgs a) {
         const auto br = token_row(mb, in_range[mb]);
         rows[mb] = br.y;
     }
-    auto load_step = [&](int mb, int hp, int buf) { load_tables(nw, rows[mb], hp, buf); };
+    auto load_step = [&](int mb, int hp, int buf) { load_tables(rows[mb], hp, buf); };
 
 #pragma unroll
     for (int mb = 0; mb < 8; ++mb) {
@@ -586,7 +592,7 @@ void fused_qkv_kernel(FusedArgs a) {
                     const f32x4 cv = Cb[cur][u], sv = Sb[cur][u];
 #pragma unroll
                     for (int t = 0; t < 2; ++t) {
-                        const f32x4 wt = Wb[cur][2 * u + t];
+                        const f32x4 wt = Wf[hp][2 * u + t];
 #pragma unroll
                         for (int gp = 0; gp < 2; ++gp) {
                             const float z0 = v[t][2 * gp] * (inv * wt[2 * gp]);
@@ -604,7 +610,7 @@ void fused_qkv_kernel(FusedArgs a) {
                 // 32 hp + 8 fg + 4 t + r
 #pragma unroll
                 for (int t = 0; t < 2; ++t) {
-                    const f32x4 wl_ = Wb[cur][t], wh_ = Wb[cur][2 + t];
+                    const f32x4 wl_ = Wf[hp][t], wh_ = Wf[hp][2 + t];
                     const f32x4 cv = Cb[cur][t], sv = Sb[cur][t];
 #pragma unroll
                     for (int r = 0; r < 4; ++r) {
