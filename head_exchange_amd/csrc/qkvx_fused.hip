@@ -479,9 +479,10 @@ void fused_qkv_kernel(FusedArgs a) {
         if (p == 2) return;
         const int m_tile = m0 + wm * 128 + mfma_row(0, fi);
         const int m = m_tile < a.M ? m_tile : a.M - 1;
-        const int s = m - (m / a.s_local) * a.s_local;
+        uint32_t bidx, s;
+        a.div_s.divmod(uint32_t(m), bidx, s);
         load_weights(p == 0 ? a.wq : a.wk);
-        load_tables(a.row0 + s, 0, 0);
+        load_tables(a.row0 + int(s), 0, 0);
     };
 
     auto epilogue = [&](int m0, int n0) {
@@ -499,9 +500,9 @@ void fused_qkv_kernel(FusedArgs a) {
         const int m_tile = m0 + wm * 128 + mfma_row(mb, fi);
         in_range = m_tile < a.M;
         const int m = in_range ? m_tile : a.M - 1;
-        const int bidx = m / a.s_local;
-        const int s = m - bidx * a.s_local;
-        return make_int2(bidx, a.row0 + s);   // batch, sequence row == position
+        uint32_t bidx, s;
+        a.div_s.divmod(uint32_t(m), bidx, s);
+        return make_int2(int(bidx), a.row0 + int(s));   // batch, sequence row == position
     };
     // Stores of one m-block: out[H] holds dims 32 H + 8 fg .. + 7 of this
     // lane's token, at byte 64 H + 16 fg of its 256-byte head vector.
@@ -546,11 +547,12 @@ void fused_qkv_kernel(FusedArgs a) {
 
     // the weights and step 0 (m-block 0, half 0) of the table are already
     // loaded (first_tables)
-    int rows[8];
+    int rows[8], bats[8];
     bool in_range[8];
 #pragma unroll
     for (int mb = 0; mb < 8; ++mb) {
         const auto br = token_row(mb, in_range[mb]);
+        bats[mb] = br.x;
         rows[mb] = br.y;
     }
     auto load_step = [&](int mb, int hp, int buf) { load_tables(rows[mb], hp, buf); };
@@ -626,8 +628,7 @@ void fused_qkv_kernel(FusedArgs a) {
             __builtin_amdgcn_sched_barrier(0);
         }
         // this block's stores go out after the next block's first loads
-        const auto br = token_row(mb, in_range[mb]);
-        uint16_t* orow = dbase + int64_t(br.x) * a.stride_b + int64_t(br.y) * a.stride_s;
+        uint16_t* orow = dbase + int64_t(bats[mb]) * a.stride_b + int64_t(rows[mb]) * a.stride_s;
         store_block(orow, in_range[mb], out);
         __builtin_amdgcn_sched_barrier(0);
     }
@@ -759,6 +760,7 @@ hipError_t launch_fused(const FusedArgs& a_in, hipStream_t stream) {
     a.tiles_m = (a.M + BM - 1) / BM;
     a.tiles_n = (a.N + BN - 1) / BN;
     a.group_m = GROUP_M;
+    a.div_s = FastDiv(uint32_t(a.s_local));
     const int tiles = a.tiles_m * a.tiles_n;
     // with readiness words one CU per XCD stays free, so that wait kernels on
     // other streams always find room while this grid runs

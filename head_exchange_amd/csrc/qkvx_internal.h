@@ -63,6 +63,7 @@ struct FusedArgs {
     int32_t tiles_m, tiles_n;
     int32_t group_m;          // tile-row group of the tile order
     int32_t rope_interleaved; // 0: pairs (i, i + 64); 1: pairs (2i, 2i + 1)
+    FastDiv div_s;            // by s_local: token -> (batch, sequence row); set at launch
     float eps;
     // Readiness words (null: not published).  ready[d] grows by 2 for every
     // (m-tile, head of destination d) stored, after the stores are released
