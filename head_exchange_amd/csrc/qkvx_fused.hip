@@ -288,7 +288,7 @@ void fused_qkv_kernel(FusedArgs a) {
     // multiplied, each replaced by the next sub-step's block right after its
     // last MFMA, and the eight X blocks (B operand) in two sets, the current
     // sub-step's and the next one's
-    bf16x8 fa[8], fb[2][8];
+    bf16x8 fa[7], w7[2], fb[2][8];
 
     // One MFMA on accumulator (nb, mb); `init`: the tile's first product, with
     // a zero accumulator input (no separate zeroing).
@@ -351,11 +351,12 @@ void fused_qkv_kernel(FusedArgs a) {
     // previous K-step's sub-step 1 (its fragments are in registers) and reads
     // sub-step 0 of K-step kt; phase 1 multiplies sub-step 0 and reads
     // sub-step 1.  In a phase, X block k of the next sub-step is read after
-    // slot 8 k + 3 (into the other X set) and W block k after slot 8 k + 7, the
-    // last MFMA of the current W block k (block 7: after the phase).  Slot mb
-    // of the first row of MFMAs of a phase waits for X block mb and W block 0
-    // of the previous phase's reads, and W block 7 is waited for before slot 8
-    // (two reads issued since).  Loads go after slots
+    // slot 2 k + 1 (into the other X set) and W block k < 7 after slot 8 k + 7,
+    // the last MFMA of the current W block k; W block 7, read into the other
+    // of its two buffers, goes first, after slot 0.  So the last read of a
+    // phase (W block 6) leaves eight slots before the step's closing wait.
+    // Slot mb of the first row of MFMAs of a phase waits for X block mb and W
+    // block 0 of the previous phase's reads, and slot 8 for all of them.  Loads go after slots
     // 8 k + 5: in steady steps the X half of K-step kt+1 in phase 0 and the W
     // half of K-step kt+2 in phase 1, into the two buffers K-step kt-1 used; in
     // a tile's first step (phase 1 only) all 16, after slots 8 k + 1 and 8 k + 5.
@@ -379,23 +380,24 @@ void fused_qkv_kernel(FusedArgs a) {
             for (int nb = 0; nb < 8; ++nb) {
 #pragma unroll
                 for (int mb = 0; mb < 8; ++mb) {
-                    // row 0 waits for exactly the reads it uses: X block mb and
-                    // W block 0 of the previous phase (in read order X0, W0,
-                    // X1, W1, ..., X7, W7; this phase's X0 follows slot 3);
-                    // slot 8 waits for W block 7 (two reads issued since)
+                    // Row 0 waits for exactly the reads it uses, W block 0 and X
+                    // block mb of the previous phase, whose reads went out in
+                    // the order W7, X0..X3, W0, X4..X7, W1..W6 (W7 after slot 0,
+                    // X k after slot 2k+1, W k after slot 8k+7); by slot 8 the
+                    // previous phase's reads are all waited for.
                     if (nb == 0) {
-                        if (mb == 0) wait_lgkm<14>();
-                        if (mb == 1) wait_lgkm<13>();
-                        if (mb == 2) wait_lgkm<11>();
-                        if (mb == 3) wait_lgkm<9>();
-                        if (mb == 4) wait_lgkm<8>();
-                        if (mb == 5) wait_lgkm<6>();
-                        if (mb == 6) wait_lgkm<4>();
-                        if (mb == 7) wait_lgkm<2>();
+                        if (mb == 0) wait_lgkm<10>();
+                        if (mb == 1) wait_lgkm<11>();
+                        if (mb == 2 || mb == 3 || mb == 4) wait_lgkm<12>();
+                        if (mb == 5 || mb == 6) wait_lgkm<11>();
+                        if (mb == 7) wait_lgkm<10>();
                     }
-                    if (nb == 1 && mb == 0) wait_lgkm<2>();
-                    mfma1(nb, mb, fa[nb], ph ? fb[0][mb] : fb[1][mb], init);
-                    if (mb == 3) lds_read(ph ? fb[1][nb] : fb[0][nb], xa, nb);
+                    if (nb == 1 && mb == 0) wait_lgkm<6>();
+                    const bf16x8& wfr = nb < 7 ? fa[nb] : (ph ? w7[0] : w7[1]);
+                    mfma1(nb, mb, wfr, ph ? fb[0][mb] : fb[1][mb], init);
+                    const int j = 8 * nb + mb;
+                    if (j == 0) lds_read(ph ? w7[1] : w7[0], wa, 7);
+                    if ((j & 1) && j < 16) lds_read(ph ? fb[1][j >> 1] : fb[0][j >> 1], xa, j >> 1);
                     if (mb == 7 && nb < 7) lds_read(fa[nb], wa, nb);
                     if (mb == 5 || (init && mb == 1)) {
                         const int v = init ? (nb * 2 + (mb == 5 ? 1 : 0)) : (ph * 8 + nb);
@@ -404,14 +406,18 @@ void fused_qkv_kernel(FusedArgs a) {
                     }
                 }
             }
-            lds_read(fa[7], wa, 7);
         };
         if (first_of_tile) {
+            // sub-step 0 in the order a phase reads it (W block 7 into the
+            // buffer phase 1 multiplies)
+            lds_read(w7[0], wb + wl[0], 7);
 #pragma unroll
-            for (int k = 0; k < 8; ++k) {
-                lds_read(fb[0][k], xb + xl[0], k);
-                lds_read(fa[k], wb + wl[0], k);
-            }
+            for (int k = 0; k < 4; ++k) lds_read(fb[0][k], xb + xl[0], k);
+            lds_read(fa[0], wb + wl[0], 0);
+#pragma unroll
+            for (int k = 4; k < 8; ++k) lds_read(fb[0][k], xb + xl[0], k);
+#pragma unroll
+            for (int k = 1; k < 7; ++k) lds_read(fa[k], wb + wl[0], k);
             phase(1, true);
         } else {
             phase(0, false);
@@ -656,7 +662,7 @@ void fused_qkv_kernel(FusedArgs a) {
 #pragma unroll
         for (int nb = 0; nb < 8; ++nb)
 #pragma unroll
-            for (int mb = 0; mb < 8; ++mb) mfma1(nb, mb, fa[nb], fb[1][mb], false);
+            for (int mb = 0; mb < 8; ++mb) mfma1(nb, mb, nb < 7 ? fa[nb] : w7[1], fb[1][mb], false);
         // the nops give the last MFMAs' results the wait states an accumulator
         // read needs
         asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
