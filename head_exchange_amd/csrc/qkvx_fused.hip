@@ -54,8 +54,9 @@
 //    XCDs' ranges), and all XCDs finish together.
 //  * Epilogue: Q/K norm and RoPE in registers, with the weights and cos/sin
 //    values loaded one step ahead (the first before the tile's last K-step);
-//    each store instruction writes whole 64-byte runs, and an m-block's stores
-//    go out together.
+//    lanes of tokens 16 apart trade pieces so that each (nontemporal) store
+//    instruction writes whole 128-byte lines, and an m-block's stores go out
+//    together.
 #include "qkvx_internal.h"
 
 namespace qkvx {
@@ -136,6 +137,11 @@ __device__ __forceinline__ void store_stream(uint16_t* p, const uint4& v) {
     typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
     const u32x4_t t = {v.x, v.y, v.z, v.w};
     __builtin_nontemporal_store(t, reinterpret_cast<u32x4_t*>(p));
+}
+
+// The value of lane fi ^ 8 of this lane's 16-lane row (DPP row rotate by 8).
+__device__ __forceinline__ unsigned int swap8(unsigned int v) {
+    return unsigned(__builtin_amdgcn_update_dpp(0, int(v), 0x128, 0xf, 0xf, false));
 }
 
 // Accumulators are read with explicit v_accvgpr_read so that the compiler
@@ -455,8 +461,8 @@ void fused_qkv_kernel(FusedArgs a) {
     // loaded while the previous half is computed; a Q/K m-block's stores go
     // out after the next block's first loads.  Vector memory operations retire
     // in order, so a wait for loads also waits for every older store: stores
-    // are therefore grouped (one group per m-block) and made of whole 64-byte
-    // runs.
+    // are therefore grouped (one group per m-block) and made of whole
+    // 128-byte lines.
     // Step (mb, hp), hp = 0, 1, covers dims 32 hp + 8 fg + 0..7 (n-blocks
     // 2 hp, 2 hp + 1) and their partners 64 further on (n-blocks 2 hp + 4,
     // 2 hp + 5).  It needs 4 weight vectors, the same for every m-block (loaded
@@ -520,12 +526,32 @@ void fused_qkv_kernel(FusedArgs a) {
         return make_int2(int(bidx), a.row0 + int(s));   // batch, sequence row == position
     };
     // Stores of one m-block: out[H] holds dims 32 H + 8 fg .. + 7 of this
-    // lane's token, at byte 64 H + 16 fg of its 256-byte head vector.
-    auto store_block = [&](uint16_t* orow, bool in_range, const uint4* out) {
-        if (!in_range) return;
+    // lane's token, at byte 64 H + 16 fg of its 256-byte head vector.  Lanes
+    // fi and fi ^ 8 (tokens 16 apart) trade one piece of each pair H = 2P,
+    // 2P + 1, so that every store instruction writes whole 128-byte lines:
+    // the first store of a pair writes both halves of line P for the tokens of
+    // lanes fi < 8, the second for those of lanes fi >= 8.  Written as 64-byte
+    // halves from two instructions, nontemporal lines leave the L2 as two
+    // partial writes.
+    // off: the token row's element offset from dbase.
+    auto store_block = [&](int64_t off, bool in_range, const uint4* out) {
+        const bool low = fi < 8;
+        const uint64_t own = uint64_t(off);
+        const uint64_t other = uint64_t(swap8(uint32_t(own))) |
+                               (uint64_t(swap8(uint32_t(own >> 32))) << 32);
+        uint16_t* orow = dbase + off;
+        uint16_t* prow = dbase + int64_t(other);
+        const bool pin = swap8(in_range ? 1u : 0u) != 0u;
 #pragma unroll
-        for (int H = 0; H < 4; ++H)
-            store_stream(orow + 32 * H + 8 * fg, out[H]);
+        for (int P = 0; P < 2; ++P) {
+            const uint4 x0 = out[2 * P], x1 = out[2 * P + 1];
+            uint4 s = low ? x1 : x0;
+            s.x = swap8(s.x); s.y = swap8(s.y); s.z = swap8(s.z); s.w = swap8(s.w);
+            uint16_t* pa = low ? orow + 64 * P + 8 * fg : prow + 64 * P + 32 + 8 * fg;
+            uint16_t* pb = low ? prow + 64 * P + 8 * fg : orow + 64 * P + 32 + 8 * fg;
+            if (low ? in_range : pin) store_stream(pa, low ? x0 : s);
+            if (low ? pin : in_range) store_stream(pb, low ? s : x1);
+        }
     };
     // eight consecutive dims (n-blocks 2H and 2H+1) -> one 16-byte piece
     auto pack8 = [&](const float (&v)[2][4]) {
@@ -543,7 +569,7 @@ void fused_qkv_kernel(FusedArgs a) {
         for (int mb = 0; mb < 8; ++mb) {
             bool in_range;
             const auto br = token_row(mb, in_range);
-            uint16_t* orow = dbase + int64_t(br.x) * a.stride_b + int64_t(br.y) * a.stride_s;
+            const int64_t off = int64_t(br.x) * a.stride_b + int64_t(br.y) * a.stride_s;
             uint4 out[4];
 #pragma unroll
             for (int H = 0; H < 4; ++H) {
@@ -554,7 +580,7 @@ void fused_qkv_kernel(FusedArgs a) {
                     for (int r = 0; r < 4; ++r) v[t][r] = acc_read(acc[2 * H + t][mb][r]);
                 out[H] = pack8(v);
             }
-            store_block(orow, in_range, out);
+            store_block(off, in_range, out);
         }
         __builtin_amdgcn_sched_barrier(0);
         return;
@@ -643,8 +669,8 @@ void fused_qkv_kernel(FusedArgs a) {
             __builtin_amdgcn_sched_barrier(0);
         }
         // this block's stores go out after the next block's first loads
-        uint16_t* orow = dbase + int64_t(bats[mb]) * a.stride_b + int64_t(rows[mb]) * a.stride_s;
-        store_block(orow, in_range[mb], out);
+        store_block(int64_t(bats[mb]) * a.stride_b + int64_t(rows[mb]) * a.stride_s, in_range[mb],
+                    out);
         __builtin_amdgcn_sched_barrier(0);
     }
     __builtin_amdgcn_sched_barrier(0);
