@@ -120,6 +120,19 @@ int check_peers(const qkvx_peers* p, const char* name, int world, int64_t batch,
     return QKVX_OK;
 }
 
+// Two peers with one base (and the shared strides) would receive into the same
+// elements, so the result would depend on which store lands last.  Peers that
+// are disjoint interleaved views of one tensor (different bases, overlapping
+// address intervals) are legitimate and not detected here.
+int check_distinct_bases(void* const* base, int world, const char* name) {
+    for (int u = 0; u < world; ++u)
+        for (int w = u + 1; w < world; ++w)
+            if (base[u] == base[w])
+                return fail(QKVX_ERR_ALIAS, "%s[%d] and %s[%d] are the same buffer", name, u, name,
+                            w);
+    return QKVX_OK;
+}
+
 // Byte range of the elements a call touches in peer u.
 Range peers_touched(const qkvx_peers* p, int u, int64_t batch, int64_t s, int head_count,
                     int64_t inner) {
@@ -425,10 +438,6 @@ int qkvx_describe(const qkvx_session* s, char* buf, size_t len) {
 }
 
 // ===========================================================================
-// head-chunk transport
-// ===========================================================================
-
-// ===========================================================================
 // readiness words
 // ===========================================================================
 
@@ -492,6 +501,10 @@ int qkvx_ready_expected(const qkvx_session* s, unsigned long long* words) {
     return ok();
 }
 
+// ===========================================================================
+// head-chunk transport
+// ===========================================================================
+
 static int check_view(const qkvx_view4* v, const char* name) {
     if (!v) return fail(QKVX_ERR_INVALID, "%s is NULL", name);
     if (!v->base) return fail(QKVX_ERR_INVALID, "%s.base is NULL", name);
@@ -546,6 +559,8 @@ int ulysses_pack_qkv_head_chunk(const qkvx_view4* q, const qkvx_view4* k, const 
     int st = check_schedule(schedule, n_chunks, chunk, hl, &off, &hc);
     if (st) return st;
     st = check_peers(dst, "dst", world, B, S, hc, 3 * QKVX_HEAD_DIM);
+    if (st) return st;
+    st = check_distinct_bases(dst->base, world, "dst.base");
     if (st) return st;
     const int64_t total = B * S * hc * 48;
     if (total >= kInt32Limit)
@@ -655,6 +670,8 @@ static int band_to_peers(const qkvx_view4* x, int world, const qkvx_peers* dst, 
     }
     st = check_peers(dst, "dst", world, B, S, int(HC), QKVX_HEAD_DIM);
     if (st) return st;
+    st = check_distinct_bases(dst->base, world, "dst.base");
+    if (st) return st;
     const int64_t total = B * S * HC * 16;
     if (total >= kInt32Limit)
         return fail(QKVX_ERR_INT32_RANGE, "%lld vectors per peer exceed 2^31", (long long)total);
@@ -711,6 +728,8 @@ int ulysses_exchange_chunks(const void* x, int world, int64_t chunk_bytes, int r
         if (!dst[u]) return fail(QKVX_ERR_INVALID, "dst[%d] is NULL", u);
         vec16 = vec16 && aligned16(dst[u]);
     }
+    const int distinct = check_distinct_bases(dst, world, "dst");
+    if (distinct) return distinct;
     const int64_t items = vec16 ? chunk_bytes / 16 : chunk_bytes;
     if (items >= kInt32Limit)
         return fail(QKVX_ERR_INT32_RANGE, "chunk of %lld bytes exceeds the per-peer limit",

@@ -207,6 +207,7 @@ def good_pack_args():
     (lambda a: setattr(a["dst"], "world", 4), -1),
     (lambda a: a["dst"].base.__setitem__(1, SRC[1] + 4096 - 64 * 1536 * 2), -5),  # rows land in k
     (lambda a: a["dst"].base.__setitem__(0, 0), -1),
+    (lambda a: a["dst"].base.__setitem__(1, DST[0]), -5),   # both peers receive into one buffer
     (lambda a: a["q"].shape.__setitem__(1, 0), -1),         # empty: no tokens
     (lambda a: [t.shape.__setitem__(0, 0) for t in (a["q"], a["k"], a["v"])], -1),  # no batch
 ])
@@ -278,6 +279,7 @@ def band_call(lib, name, x, world, dst):
     (lambda a: a["dst"].base.__setitem__(1, SRC[0] + 4096), -5),   # lands inside x
     (lambda a: a["dst"].base.__setitem__(0, 0), -1),
     (lambda a: a["dst"].base.__setitem__(0, DST[0] + 8), -4),
+    (lambda a: a["dst"].base.__setitem__(1, DST[0]), -5),    # both peers receive into one buffer
     (lambda a: a["x"].shape.__setitem__(1, 0), -1),          # empty: no rows
     (lambda a: a["x"].shape.__setitem__(2, 0), -1),          # empty: no heads
 ])
@@ -310,6 +312,7 @@ def exchange(lib, x, world, chunk, rank, dsts):
     (dict(chunk=0), -1),
     (dict(dsts=[DST[0], 0]), -1),
     (dict(dsts=[DST[0], SRC[0]]), -5),         # slot 0 of peer 1 is x itself
+    (dict(dsts=[DST[0], DST[0]]), -5),         # both peers receive into one buffer
     (dict(chunk=1 << 31, x=FAKE + 1), -6),     # byte path: 2^31 items
 ])
 def test_exchange_rejects(lib, kw, status):
