@@ -122,6 +122,27 @@ def test_small_full_slots(gpu_lib, wl):
     check_full(views, inp, wl.rank, wl.name)
 
 
+# Token counts under one tile, so the tile holds tokens past M: the epilogue
+# pairs lanes whose tokens are 16 apart for its line-wide stores, and these
+# counts end the shard at every kind of position within a 32-token group
+# (both partners in range, only the lower one, neither).  From 256 tokens on
+# the last tile row is moved back to end at M and no token is out of range.
+TAIL_M = [1, 8, 15, 16, 17, 24, 31, 33, 48, 100, 129, 255]
+
+
+@pytest.mark.parametrize("m", TAIL_M)
+def test_tail_tokens_under_one_tile(gpu_lib, m):
+    wl = W.custom(40 + m, batch=1, s_local=m, heads=2, world=2, rank=1,
+                  layout="fused" if m % 2 else "bshd", schedule=(1,), rope_base=1e4)
+    rope = "interleaved" if m % 3 == 0 else "rotate_half"
+    inp = Inputs(wl)
+    sess = make_session(gpu_lib, wl, rope=rope)
+    sess.poison_receive_slots()
+    views = run(sess, inp)
+    torch.cuda.synchronize()
+    check_full(views, inp, wl.rank, f"{wl.name}:M{m}:{rope}", rope=rope)
+
+
 @pytest.mark.parametrize("wl", SMALL[:3], ids=lambda w: w.name)
 def test_small_full_slots_interleaved_rope(gpu_lib, wl):
     """The pages' pairing (2i, 2i+1) selected at session creation."""
