@@ -509,21 +509,27 @@ def main():
     merge_src = [band[:, u * S:(u + 1) * S] for u in range(U)]
     stream = torch.cuda.current_stream()
 
+    def pack_group():
+        for c in range(len(sched)):
+            hx.ulysses_pack_qkv_head_chunk(q, k, v, world=U, schedule=wl.schedule, chunk=c,
+                                           dst=pack_dst[c], row_offset=wl.rank * S, stream=stream)
+
+    def merge_group():
+        for c, (off, _) in enumerate(sched):
+            hx.ulysses_merge_output_head_chunk(merge_src, world=U, local_heads=hl,
+                                               schedule=wl.schedule, chunk=c, out=merge_out,
+                                               head_offset=off, stream=stream)
+
     def step(ev=None):
         if ev is not None:
             ev[0].record(stream)
         sess.forward(x, w, wq, wk, cs, wl.rank, stream)
         if ev is not None:
             ev[1].record(stream)
-        for c in range(len(sched)):
-            hx.ulysses_pack_qkv_head_chunk(q, k, v, world=U, schedule=wl.schedule, chunk=c,
-                                           dst=pack_dst[c], row_offset=wl.rank * S, stream=stream)
+        pack_group()
         if ev is not None:
             ev[2].record(stream)
-        for c, (off, _) in enumerate(sched):
-            hx.ulysses_merge_output_head_chunk(merge_src, world=U, local_heads=hl,
-                                               schedule=wl.schedule, chunk=c, out=merge_out,
-                                               head_offset=off, stream=stream)
+        merge_group()
         if ev is not None:
             ev[3].record(stream)
 
@@ -548,6 +554,25 @@ def main():
     merge_bytes = sum(2.0 * B * S * U * cnt * 128 * 2 for _, cnt in sched)
     achieved = flops / (fused_ms * 1e-3) / 1e12
     traffic = read_traffic()
+
+    # The same pack and merge groups REPS times back to back between one pair
+    # of events: the per-group time without the cost of the events themselves,
+    # which the per-step figures above include (a pair of timing events around
+    # one empty kernel measures about 6 us).
+    REPS = 20
+
+    def amortized_ms(group):
+        group()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(REPS):
+            group()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / REPS
+
+    pack_rep_ms, merge_rep_ms = amortized_ms(pack_group), amortized_ms(merge_group)
 
     calib = None
     if args.copy_calibration:
@@ -590,7 +615,13 @@ def main():
                       "merge_gbps": merge_bytes / (merge_ms * 1e-3) / 1e9,
                       "merge_frac": merge_bytes / (merge_ms * 1e-3) / 1e9 / PEAK_HBM_GBPS,
                       "pack_bytes": pack_bytes, "merge_bytes": merge_bytes,
-                      "peak_gbps": PEAK_HBM_GBPS},
+                      "peak_gbps": PEAK_HBM_GBPS,
+                      "back_to_back": {
+                          "groups": REPS,
+                          "pack_us": pack_rep_ms * 1e3,
+                          "pack_frac": pack_bytes / (pack_rep_ms * 1e-3) / 1e9 / PEAK_HBM_GBPS,
+                          "merge_us": merge_rep_ms * 1e3,
+                          "merge_frac": merge_bytes / (merge_rep_ms * 1e-3) / 1e9 / PEAK_HBM_GBPS}},
         "kernels_ms": {"fused": fused_ms, "pack_all_chunks": pack_ms, "merge_all_chunks": merge_ms},
         "kernels_pct": {n: pct(v) for n, v in per.items()},
     }
