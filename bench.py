@@ -234,6 +234,17 @@ def sweep(hx, torch, W, dev, reps: int = 10):
             st["frac"] = st["tflops"] / PEAK_BF16_TFLOPS
             res[f"fused_{mode}"] = st
         sess.close()
+        # the pages' RoPE pairing (2i, 2i+1): the same launch with the other
+        # epilogue branch, warm
+        sess = hx.qkvx_create(wl.hidden, H, 128, U, wl.layout, M, wl.num_slots,
+                              rope="interleaved")
+        for _ in range(3):
+            fused()
+        st = pct(launch_times(torch, fused, reps, stream, evict, None))
+        st["tflops"] = flops / (st["median_us"] * 1e-6) / 1e12
+        st["frac"] = st["tflops"] / PEAK_BF16_TFLOPS
+        res["fused_warm_interleaved_rope"] = st
+        sess.close()
         del xs, w, sess
         torch.cuda.empty_cache()
 
