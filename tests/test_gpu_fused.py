@@ -143,6 +143,34 @@ def test_tail_tokens_under_one_tile(gpu_lib, m):
     check_full(views, inp, wl.rank, f"{wl.name}:M{m}:{rope}", rope=rope)
 
 
+def random_case(seed: int):
+    """A seeded random small workload: head count (odd counts leave the last
+    256-wide tile column half empty), a world size dividing it, a rank, batch
+    and token counts under, at and above tile multiples, layout, RoPE pairing
+    and base."""
+    rng = np.random.default_rng(9000 + seed)
+    heads = int(rng.integers(1, 7))
+    world = int(rng.choice([u for u in (1, 2, 3, 4, 6) if heads % u == 0]))
+    s_local = int(rng.choice([int(rng.integers(1, 64)), 128, 256, int(rng.integers(257, 600))]))
+    batch = int(rng.integers(1, 4))
+    wl = W.custom(200 + seed, batch=batch, s_local=s_local, heads=heads, world=world,
+                  rank=int(rng.integers(0, world)), layout=str(rng.choice(["bshd", "fused"])),
+                  schedule=(heads // world,), rope_base=float(rng.choice([1e4, 1e6])))
+    return wl, str(rng.choice(["rotate_half", "interleaved"]))
+
+
+@pytest.mark.parametrize("seed", range(24))
+def test_random_small_shapes(gpu_lib, seed):
+    wl, rope = random_case(seed)
+    inp = Inputs(wl)
+    sess = make_session(gpu_lib, wl, rope=rope)
+    sess.poison_receive_slots()
+    views = run(sess, inp)
+    torch.cuda.synchronize()
+    check_full(views, inp, wl.rank, f"seed {seed} {wl.name} B{wl.batch} S{wl.s_local} "
+               f"H{wl.heads} U{wl.world} r{wl.rank} {wl.layout} {rope}", rope=rope)
+
+
 @pytest.mark.parametrize("wl", SMALL[:3], ids=lambda w: w.name)
 def test_small_full_slots_interleaved_rope(gpu_lib, wl):
     """The pages' pairing (2i, 2i+1) selected at session creation."""
