@@ -100,6 +100,24 @@ def test_gather_heads_all_ranks(gpu_lib, wl):
     check_gather(wl, bands, run_gather(gpu_lib, wl, bands))
 
 
+def random_band_case(seed: int):
+    """A seeded random group: world size (5 included), heads per rank, batch
+    and token counts."""
+    rng = np.random.default_rng(11000 + seed)
+    world = int(rng.choice([1, 2, 3, 4, 5, 8]))
+    hl = int(rng.integers(1, 5))
+    return case(300 + seed, int(rng.integers(1, 3)), int(rng.integers(1, 40)), world * hl, world)
+
+
+@pytest.mark.parametrize("seed", range(16))
+def test_random_scatter_then_gather_all_ranks(gpu_lib, seed):
+    wl = random_band_case(seed)
+    shards = W.rank_shards(wl)
+    check_scatter(wl, shards, run_scatter(gpu_lib, wl, shards))
+    bands = W.rank_bands(wl)
+    check_gather(wl, bands, run_gather(gpu_lib, wl, bands))
+
+
 def test_scatter_then_gather_is_identity_on_gpu(gpu_lib):
     """Both send halves on the GPU alone: gather(scatter(x)) returns every
     rank's input bit for bit."""
