@@ -533,7 +533,10 @@ void fused_qkv_kernel(FusedArgs a) {
     // lanes fi < 8, the second for those of lanes fi >= 8.  Written as 64-byte
     // halves from two instructions, nontemporal lines leave the L2 as two
     // partial writes.
-    // off: the token row's element offset from dbase.
+    // off: the token row's element offset from dbase.  Called with all 64
+    // lanes active (wave-uniform control flow only): the DPP moves read the
+    // partner lane's registers, and out-of-range tokens are skipped at the
+    // stores, after the trade.
     auto store_block = [&](int64_t off, bool in_range, const uint4* out) {
         const bool low = fi < 8;
         const uint64_t own = uint64_t(off);
