@@ -144,6 +144,16 @@ __device__ __forceinline__ unsigned int swap8(unsigned int v) {
     return unsigned(__builtin_amdgcn_update_dpp(0, int(v), 0x128, 0xf, 0xf, false));
 }
 
+// One DPP move with a bank mask: lanes 8-15 of each 16-lane row (banks 2, 3)
+// take v from lane fi ^ 8 and lanes 0-7 keep `keep` (take_hi); take_lo the
+// other way round.
+__device__ __forceinline__ unsigned int take_hi(unsigned int keep, unsigned int v) {
+    return unsigned(__builtin_amdgcn_update_dpp(int(keep), int(v), 0x128, 0xf, 0xc, false));
+}
+__device__ __forceinline__ unsigned int take_lo(unsigned int keep, unsigned int v) {
+    return unsigned(__builtin_amdgcn_update_dpp(int(keep), int(v), 0x128, 0xf, 0x3, false));
+}
+
 // Accumulators are read with explicit v_accvgpr_read so that the compiler
 // never copies all 256 of them into VGPRs at once (there is no room).
 __device__ __forceinline__ float acc_read(const float& a) {
@@ -540,20 +550,25 @@ void fused_qkv_kernel(FusedArgs a) {
     auto store_block = [&](int64_t off, bool in_range, const uint4* out) {
         const bool low = fi < 8;
         const uint64_t own = uint64_t(off);
-        const uint64_t other = uint64_t(swap8(uint32_t(own))) |
-                               (uint64_t(swap8(uint32_t(own >> 32))) << 32);
-        uint16_t* orow = dbase + off;
-        uint16_t* prow = dbase + int64_t(other);
+        const int64_t other = int64_t(uint64_t(swap8(uint32_t(own))) |
+                                      (uint64_t(swap8(uint32_t(own >> 32))) << 32));
         const bool pin = swap8(in_range ? 1u : 0u) != 0u;
+        // first store of a pair: low lanes their own token's dims 0..31 of the
+        // line, high lanes their partner's dims 32..63; second store: the
+        // other way round (line P is 64 P further on: an immediate offset)
+        uint16_t* pa = dbase + (low ? off : other + 32) + 8 * fg;
+        uint16_t* pb = dbase + (low ? other : off + 32) + 8 * fg;
+        const bool ina = low ? in_range : pin, inb = low ? pin : in_range;
 #pragma unroll
         for (int P = 0; P < 2; ++P) {
             const uint4 x0 = out[2 * P], x1 = out[2 * P + 1];
-            uint4 s = low ? x1 : x0;
-            s.x = swap8(s.x); s.y = swap8(s.y); s.z = swap8(s.z); s.w = swap8(s.w);
-            uint16_t* pa = low ? orow + 64 * P + 8 * fg : prow + 64 * P + 32 + 8 * fg;
-            uint16_t* pb = low ? prow + 64 * P + 8 * fg : orow + 64 * P + 32 + 8 * fg;
-            if (low ? in_range : pin) store_stream(pa, low ? x0 : s);
-            if (low ? pin : in_range) store_stream(pb, low ? s : x1);
+            uint4 a, b;
+            a.x = take_hi(x0.x, x1.x); a.y = take_hi(x0.y, x1.y);
+            a.z = take_hi(x0.z, x1.z); a.w = take_hi(x0.w, x1.w);
+            b.x = take_lo(x1.x, x0.x); b.y = take_lo(x1.y, x0.y);
+            b.z = take_lo(x1.z, x0.z); b.w = take_lo(x1.w, x0.w);
+            if (ina) store_stream(pa + 64 * P, a);
+            if (inb) store_stream(pb + 64 * P, b);
         }
     };
     // eight consecutive dims (n-blocks 2H and 2H+1) -> one 16-byte piece
