@@ -16,6 +16,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libqkvx.so")
 HEAD_DIM = 128
 MAX_WORLD = 64
+CTRL_BYTES = 1024       # QKVX_CTRL_BYTES: the session's control area, zeroed at creation
 LAYOUTS = {"bshd": 0, "fused": 1}
 ROPES = {"rotate_half": 0, "interleaved": 1}
 
@@ -180,10 +181,22 @@ def view4(t) -> View4:
     return v
 
 
-def peers(tensors: Sequence, row_offset: int = 0, head_offset: int = 0) -> Peers:
-    """``world`` equally shaped [B, rows, heads, inner] tensors as a qkvx_peers."""
+def peers(tensors: Sequence, row_offset: int = 0, head_offset: int = 0,
+          inner: Optional[int] = None) -> Peers:
+    """``world`` equally shaped [B, rows, heads, inner] tensors as a qkvx_peers.
+
+    ``inner``: the innermost length the call moves per head (128 for head
+    vectors, 384 for q|k|v records); a tensor with another innermost length is
+    rejected here, since the library sees only base pointers and strides."""
+    if len(tensors) == 0:
+        raise ValueError("at least one peer tensor is needed")
     p = Peers()
     t0 = tensors[0]
+    if t0.dim() != 4:
+        raise ValueError("peer tensors must be 4-D [B, rows, heads, inner]")
+    if inner is not None and t0.shape[3] != inner:
+        raise ValueError(f"peer tensors must have an innermost length of {inner}, "
+                         f"got {t0.shape[3]}")
     p.world = len(tensors)
     p.batch, p.rows, p.heads = t0.shape[0], t0.shape[1], t0.shape[2]
     for i in range(3):
@@ -236,6 +249,11 @@ class Session:
         device = torch.device("cuda") if device is None else torch.device(device)
         # 256-byte alignment: torch's allocator returns 512-byte aligned blocks
         self.slots = torch.empty(max(nbytes // 2, 1), dtype=torch.uint16, device=device)
+        if nbytes:
+            # the library needs its control area zero at creation (session
+            # setup: the fill is waited for here, once)
+            self.slots[:CTRL_BYTES // 2].zero_()
+            torch.cuda.synchronize(device)
         h = ctypes.c_void_p()
         _check(lib.qkvx_create(hidden, num_heads, head_dim, world, LAYOUTS[layout], ROPES[rope],
                                max_tokens, num_slots, self.slots.data_ptr(), nbytes,
@@ -267,8 +285,14 @@ class Session:
         _check_bf16(w_qkv, "w_qkv")
         _on_gpu(x, "x")
         _on_gpu(w_qkv, "w_qkv")
-        if x.dim() != 3 or not x.is_contiguous() or not w_qkv.is_contiguous():
-            raise ValueError("x must be a contiguous [B, S_local, hidden] tensor and w_qkv contiguous")
+        # the library reads batch*s_local*hidden elements of x and 3*hidden*hidden
+        # of w_qkv from their base pointers: their shapes are checked here
+        if x.dim() != 3 or not x.is_contiguous() or x.shape[2] != self.hidden:
+            raise ValueError(f"x must be a contiguous [B, S_local, {self.hidden}] tensor, "
+                             f"got {tuple(x.shape)}")
+        if tuple(w_qkv.shape) != (3 * self.hidden, self.hidden) or not w_qkv.is_contiguous():
+            raise ValueError(f"w_qkv must be a contiguous [{3 * self.hidden}, {self.hidden}] "
+                             f"tensor, got {tuple(w_qkv.shape)}")
         _check_f32(q_norm_w, "q_norm_w", 128)
         _check_f32(k_norm_w, "k_norm_w", 128)
         _check_f32(cos_sin, "cos_sin", 0)
@@ -359,7 +383,9 @@ def ulysses_pack_qkv_head_chunk(q, k, v, *, world: int, schedule: Sequence[int],
     ([B, rows, heads, 384]) at rows ``row_offset..`` and heads ``head_offset..``."""
     sched, n = _schedule(schedule)
     vq, vk, vv = view4(q), view4(k), view4(v)
-    pd = peers(dst, row_offset, head_offset)
+    if len(dst) != world:
+        raise ValueError(f"expected {world} destinations, got {len(dst)}")
+    pd = peers(dst, row_offset, head_offset, inner=3 * HEAD_DIM)
     _check(load().ulysses_pack_qkv_head_chunk(ctypes.byref(vq), ctypes.byref(vk), ctypes.byref(vv),
                                               world, sched, n, chunk, ctypes.byref(pd),
                                               _stream(stream)))
@@ -374,10 +400,16 @@ def ulysses_merge_output_head_chunk(src: Sequence, *, world: int, local_heads: i
     ``out`` ([B, S, world*local_heads, 128], contiguous)."""
     _check_bf16(out, "out")
     _on_gpu(out, "out")
-    if out.dim() != 4 or not out.is_contiguous():
-        raise ValueError("out must be a contiguous [B, S_local, H, 128] tensor")
+    # the kernel writes [B, S_local, world*local_heads, 128] from out's base:
+    # out must have exactly that shape
+    if out.dim() != 4 or not out.is_contiguous() or out.shape[2] != world * local_heads \
+            or out.shape[3] != HEAD_DIM:
+        raise ValueError(f"out must be a contiguous [B, S_local, {world * local_heads}, "
+                         f"{HEAD_DIM}] tensor, got {tuple(out.shape)}")
+    if len(src) != world:
+        raise ValueError(f"expected {world} sources, got {len(src)}")
     sched, n = _schedule(schedule)
-    ps = peers(src, row_offset, head_offset)
+    ps = peers(src, row_offset, head_offset, inner=HEAD_DIM)
     _check(load().ulysses_merge_output_head_chunk(ctypes.byref(ps), world, local_heads, sched, n,
                                                   chunk, out.data_ptr(), out.shape[0],
                                                   out.shape[1], _stream(stream)))
@@ -392,7 +424,9 @@ def ulysses_merge_output_head_chunk(src: Sequence, *, world: int, local_heads: i
 def _band_to_peers(fn_name: str, x, world: int, dst: Sequence, row_offset: int,
                    head_offset: int, stream) -> None:
     vx = view4(x)
-    pd = peers(dst, row_offset, head_offset)
+    if len(dst) != world:
+        raise ValueError(f"expected {world} destinations, got {len(dst)}")
+    pd = peers(dst, row_offset, head_offset, inner=HEAD_DIM)
     _check(getattr(load(), fn_name)(ctypes.byref(vx), world, ctypes.byref(pd), _stream(stream)))
 
 

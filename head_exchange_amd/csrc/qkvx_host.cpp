@@ -153,14 +153,16 @@ struct qkvx_session {
     int hidden, heads, world, layout, rope, num_slots;
     int64_t max_tokens;
     int64_t region_elems;       // max_tokens * 3 * hidden
-    uint16_t* slots;            // num_slots * world regions
-    size_t slot_bytes;
+    uint8_t* memory;            // control area + num_slots * world regions
+    uint16_t* slots;            // memory + QKVX_CTRL_BYTES
+    size_t slot_bytes;          // bytes of memory
     bool owns_slots;
     bool publish;                      // forward calls publish readiness words
     bool last_published;               // the last call did
-    unsigned long long* ready;         // device: QKVX_MAX_WORLD readiness words
-    int* timeouts;                     // device: wait-kernel timeout counter
-    unsigned int* sched;               // device: tile-claim counters (first forward call)
+    // device words in the control area (zero at creation)
+    unsigned long long* ready;         // QKVX_MAX_WORLD readiness words
+    int* timeouts;                     // wait-kernel timeout counter
+    unsigned int* sched;               // kSchedWords tile-claim counters
     unsigned long long expect[QKVX_MAX_WORLD];   // word values after the last publishing call
     int64_t calls;              // successful forward calls so far
     bool has_last;
@@ -173,7 +175,8 @@ const char* qkvx_last_error(void) { return g_error.c_str(); }
 
 size_t qkvx_slot_bytes(int hidden, int world, int64_t max_tokens, int num_slots) {
     if (hidden <= 0 || world <= 0 || max_tokens <= 0 || num_slots <= 0) return 0;
-    return size_t(num_slots) * size_t(world) * size_t(max_tokens) * 3u * size_t(hidden) * 2u;
+    return size_t(QKVX_CTRL_BYTES) +
+           size_t(num_slots) * size_t(world) * size_t(max_tokens) * 3u * size_t(hidden) * 2u;
 }
 
 int qkvx_create(int hidden, int num_heads, int head_dim, int world, int layout, int rope,
@@ -222,8 +225,14 @@ int qkvx_create(int hidden, int num_heads, int head_dim, int world, int layout, 
         if (reinterpret_cast<uintptr_t>(slot_memory) & 255u)
             return fail(QKVX_ERR_ALIGNMENT, "slot_memory is not 256-byte aligned");
     } else {
+        // session setup: allocate, and zero the control area once (synchronously)
         hipError_t e = hipMalloc(&slot_memory, need);
         if (e != hipSuccess) return hip_fail(e, "hipMalloc of the receive slots");
+        e = hipMemset(slot_memory, 0, QKVX_CTRL_BYTES);
+        if (e != hipSuccess) {
+            (void)hipFree(slot_memory);      // the memset error is the one reported
+            return hip_fail(e, "zeroing the session's control area");
+        }
         slot_bytes = need;
         owns = true;
     }
@@ -236,16 +245,17 @@ int qkvx_create(int hidden, int num_heads, int head_dim, int world, int layout, 
     s->num_slots = num_slots;
     s->max_tokens = max_tokens;
     s->region_elems = region;
-    s->slots = static_cast<uint16_t*>(slot_memory);
+    s->memory = static_cast<uint8_t*>(slot_memory);
+    s->slots = reinterpret_cast<uint16_t*>(s->memory + QKVX_CTRL_BYTES);
     s->slot_bytes = slot_bytes;
     s->owns_slots = owns;
     s->calls = 0;
     s->has_last = false;
     s->publish = false;
     s->last_published = false;
-    s->ready = nullptr;
-    s->timeouts = nullptr;
-    s->sched = nullptr;
+    s->ready = reinterpret_cast<unsigned long long*>(s->memory + kCtrlReady);
+    s->timeouts = reinterpret_cast<int*>(s->memory + kCtrlTimeouts);
+    s->sched = reinterpret_cast<unsigned int*>(s->memory + kCtrlSched);
     memset(s->expect, 0, sizeof(s->expect));
     *out = s;
     return ok();
@@ -264,9 +274,7 @@ int qkvx_destroy(qkvx_session* s) {
             what = name;
         }
     };
-    release(s->ready, "hipFree of the readiness words");
-    release(s->sched, "hipFree of the tile-claim counters");
-    if (s->owns_slots) release(s->slots, "hipFree of the receive slots");
+    if (s->owns_slots) release(s->memory, "hipFree of the receive slots");
     delete s;
     if (first != hipSuccess) return hip_fail(first, what);
     return ok();
@@ -324,7 +332,7 @@ int qkvx_forward(qkvx_session* s, const void* x, int batch, int s_local, const v
         return fail(QKVX_ERR_ALIGNMENT,
                     "cos_sin and the norm weights must start at 16-byte aligned addresses");
     const int64_t hidden = s->hidden;
-    const Range slots = bytes_range(s->slots, int64_t(s->slot_bytes));
+    const Range slots = bytes_range(s->memory, int64_t(s->slot_bytes));
     const Range ins[5] = {bytes_range(x, M * hidden * 2), bytes_range(w_qkv, 3 * hidden * hidden * 2),
                           bytes_range(q_norm_w, 512), bytes_range(k_norm_w, 512),
                           bytes_range(cos_sin, cos_sin_rows * 512)};
@@ -365,21 +373,8 @@ int qkvx_forward(qkvx_session* s, const void* x, int batch, int s_local, const v
         a.dest_cols = (hl % 2 == 0 && hidden % 256 == 0) ? hl / 2 : 0;
         a.part_cols = int32_t(hidden / 256);
     }
-    {
-        if (!s->sched) {
-            // zeroed once, synchronously; every launch leaves them zero again
-            void* mem = nullptr;
-            hipError_t e = hipMalloc(&mem, kSchedWords * sizeof(unsigned int));
-            if (e == hipSuccess) e = hipMemset(mem, 0, kSchedWords * sizeof(unsigned int));
-            if (e == hipSuccess) e = hipDeviceSynchronize();
-            if (e != hipSuccess) {
-                if (mem) (void)hipFree(mem);   // the allocation error is the one reported
-                return hip_fail(e, "allocation of the tile-claim counters");
-            }
-            s->sched = static_cast<unsigned int*>(mem);
-        }
-        a.sched = s->sched;
-    }
+    // zero since the session was created; every launch leaves them zero again
+    a.sched = s->sched;
     hipError_t e = launch_fused(a, static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return hip_fail(e, "fused projection launch");
     s->calls += 1;
@@ -443,20 +438,7 @@ int qkvx_describe(const qkvx_session* s, char* buf, size_t len) {
 
 int qkvx_set_publish(qkvx_session* s, int enable) {
     if (!s) return fail(QKVX_ERR_INVALID, "session is NULL");
-    if (enable && !s->ready) {
-        // words and the timeout counter in one allocation, zeroed once
-        void* mem = nullptr;
-        const size_t bytes = sizeof(unsigned long long) * QKVX_MAX_WORLD + 256;
-        hipError_t e = hipMalloc(&mem, bytes);
-        if (e == hipSuccess) e = hipMemset(mem, 0, bytes);
-        if (e != hipSuccess) {
-            if (mem) (void)hipFree(mem);   // the allocation error is the one reported
-            return hip_fail(e, "allocation of the readiness words");
-        }
-        s->ready = static_cast<unsigned long long*>(mem);
-        s->timeouts = reinterpret_cast<int*>(static_cast<char*>(mem) +
-                                             sizeof(unsigned long long) * QKVX_MAX_WORLD);
-    }
+    // the words live in the session's control area: host bookkeeping only
     s->publish = enable != 0;
     return ok();
 }
@@ -484,7 +466,6 @@ int qkvx_wait_ready(qkvx_session* s, int dest, int spin_limit, void* stream) {
 
 int qkvx_ready_state(qkvx_session* s, unsigned long long* words, int* timeouts) {
     if (!s) return fail(QKVX_ERR_INVALID, "session is NULL");
-    if (!s->ready) return fail(QKVX_ERR_INVALID, "readiness words were never enabled");
     hipError_t e = hipSuccess;
     if (words)
         e = hipMemcpy(words, s->ready, sizeof(unsigned long long) * s->world,

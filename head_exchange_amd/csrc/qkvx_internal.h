@@ -81,6 +81,14 @@ struct FusedArgs {
 
 constexpr int kSchedWords = 16;   // tile-claim counter words a session keeps
 
+// Byte offsets of a session's device words in the control area at the start of
+// its slot memory (QKVX_CTRL_BYTES, zero when the session is created).
+constexpr int kCtrlReady = 0;                                  // QKVX_MAX_WORLD x uint64
+constexpr int kCtrlTimeouts = 8 * QKVX_MAX_WORLD;              // int
+constexpr int kCtrlSched = kCtrlTimeouts + 64;                 // kSchedWords x uint32
+static_assert(kCtrlSched + 4 * kSchedWords <= QKVX_CTRL_BYTES, "control area too small");
+static_assert(QKVX_CTRL_BYTES % 256 == 0, "receive slots must stay 256-byte aligned");
+
 // Readiness: a call adds this much to ready[d] of every destination d.
 inline unsigned long long ready_increment(int64_t M, int local_heads) {
     return (unsigned long long)((M + 255) / 256) * 6ull * (unsigned long long)local_heads;

@@ -65,7 +65,7 @@ def create(lib, hidden=512, heads=4, world=2, layout=0, max_tokens=64, slots=2,
 
 
 def test_slot_bytes(lib):
-    assert lib.qkvx_slot_bytes(7168, 4, 9472, 2) == 2 * 4 * 9472 * 3 * 7168 * 2
+    assert lib.qkvx_slot_bytes(7168, 4, 9472, 2) == 1024 + 2 * 4 * 9472 * 3 * 7168 * 2
     assert lib.qkvx_slot_bytes(0, 4, 9472, 2) == 0
 
 
@@ -330,8 +330,13 @@ def test_readiness_calls_reject(lib):
     st, h = create(lib)
     assert st == 0
     assert lib.qkvx_wait_ready(h, 0, 10, None) == -1          # no publishing call yet
-    assert lib.qkvx_set_publish(h, 0) == 0                     # disabling allocates nothing
-    assert lib.qkvx_ready_state(h, None, None) == -1           # words never enabled
+    assert lib.qkvx_set_publish(h, 0) == 0
+    # the words live in the control area of the slot memory: enabling them is
+    # host bookkeeping (no device here, so any allocation would fail)
+    assert lib.qkvx_set_publish(h, 1) == 0
+    assert lib.qkvx_wait_ready(h, 0, 10, None) == -1          # still no publishing call
+    assert lib.qkvx_set_publish(h, 0) == 0
+    assert lib.qkvx_ready_state(h, None, None) == 0            # nothing asked for
     words = (ctypes.c_ulonglong * 2)(7, 7)
     assert lib.qkvx_ready_expected(h, words) == 0 and list(words) == [0, 0]
     assert lib.qkvx_set_publish(None, 1) == -1
@@ -371,3 +376,89 @@ def test_binding_rejects_host_tensors_before_any_call():
     with pytest.raises(ValueError, match="GPU tensor"):
         hx.ulysses_exchange_chunks(torch.zeros(2, 16, dtype=torch.uint8), world=2, rank=0,
                                    dst=[torch.zeros(2, 16, dtype=torch.uint8)] * 2)
+
+
+def test_forward_path_allocates_nothing(lib):
+    """A valid call on a session built on caller memory reaches the kernel launch
+    directly: there is no device here, so the launch is what fails, not an
+    allocation or a synchronisation before it."""
+    st, h = create(lib)
+    assert st == 0
+    status = forward(lib, h)
+    msg = lib.qkvx_last_error().decode()
+    assert status == -9 and "launch" in msg, msg
+    assert "alloc" not in msg and "synchron" not in msg, msg
+    assert lib.qkvx_destroy(h) == 0
+
+
+def test_slot_bytes_include_the_control_area(lib):
+    assert hx.CTRL_BYTES == 1024
+    base = 2 * 4 * 9472 * 3 * 7168 * 2
+    assert lib.qkvx_slot_bytes(7168, 4, 9472, 2) == hx.CTRL_BYTES + base
+    # caller memory one byte short of the control area plus the regions
+    st, _ = create(lib, nbytes=lib.qkvx_slot_bytes(512, 2, 64, 2) - 1)
+    assert st == -3, lib.qkvx_last_error()
+
+
+class FakeDev:
+    """A host tensor that presents itself as a device tensor at a fake address
+    (never dereferenced): the binding's own checks run on it; a call that got
+    past them would reach the library, whose launch fails without a device."""
+
+    is_cuda = True
+
+    def __init__(self, t, ptr=FAKE):
+        self._t, self._p = t, ptr
+
+    def data_ptr(self):
+        return self._p
+
+    def __getattr__(self, name):
+        return getattr(self._t, name)
+
+
+def bf16(*shape):
+    import torch
+    return torch.zeros(*shape, dtype=torch.bfloat16)
+
+
+def test_binding_rejects_wrong_shapes_before_any_call():
+    """Shapes the C ABI cannot see (it takes base pointers and strides) are
+    checked by the binding, so a wrong one is a ValueError, not an access out
+    of bounds on the GPU."""
+    import torch
+    sess = object.__new__(hx.Session)
+    sess.hidden, sess._h = 512, None
+    f32 = lambda n: FakeDev(torch.zeros(n, dtype=torch.float32))
+    wq, cs = f32(128), FakeDev(torch.zeros(256, 128, dtype=torch.float32))
+    good_w = FakeDev(bf16(1536, 512))
+    with pytest.raises(ValueError, match="x must be"):
+        sess.forward(FakeDev(bf16(1, 64, 256)), good_w, wq, wq, cs, 0)      # hidden 256 != 512
+    with pytest.raises(ValueError, match="w_qkv must be"):
+        sess.forward(FakeDev(bf16(1, 64, 512)), FakeDev(bf16(1024, 512)), wq, wq, cs, 0)
+    with pytest.raises(ValueError, match="w_qkv must be"):
+        sess.forward(FakeDev(bf16(1, 64, 512)), FakeDev(bf16(1536, 256)), wq, wq, cs, 0)
+    # merge: out's head axis must be world * local_heads, its inner axis 128
+    src = [FakeDev(bf16(1, 8, 2, 128), FAKE + (u << 30)) for u in range(2)]
+    for shape in [(1, 8, 3, 128), (1, 8, 4, 64), (1, 8, 2, 128)]:
+        with pytest.raises(ValueError, match="out must be"):
+            hx.ulysses_merge_output_head_chunk(src, world=2, local_heads=2, schedule=[2],
+                                               chunk=0, out=FakeDev(bf16(*shape), FAKE + (9 << 30)))
+    # merge sources and pack destinations: innermost length 128 and 384
+    bad_src = [FakeDev(bf16(1, 8, 2, 384), FAKE + (u << 30)) for u in range(2)]
+    with pytest.raises(ValueError, match="innermost length of 128"):
+        hx.ulysses_merge_output_head_chunk(bad_src, world=2, local_heads=2, schedule=[2], chunk=0,
+                                           out=FakeDev(bf16(1, 8, 4, 128), FAKE + (9 << 30)))
+    q = FakeDev(bf16(1, 8, 4, 128), FAKE + (20 << 30))
+    bad_dst = [FakeDev(bf16(1, 16, 2, 128), FAKE + (u << 30)) for u in range(2)]
+    with pytest.raises(ValueError, match="innermost length of 384"):
+        hx.ulysses_pack_qkv_head_chunk(q, q, q, world=2, schedule=[2], chunk=0, dst=bad_dst)
+    with pytest.raises(ValueError, match="expected 2 destinations"):
+        hx.ulysses_pack_qkv_head_chunk(q, q, q, world=2, schedule=[2], chunk=0,
+                                       dst=[FakeDev(bf16(1, 16, 2, 384))])
+    # whole-band transforms: destinations of head vectors
+    with pytest.raises(ValueError, match="innermost length of 128"):
+        hx.ulysses_scatter_heads(q, world=2, dst=[FakeDev(bf16(1, 16, 2, 384), FAKE + (u << 30))
+                                                  for u in range(2)])
+    with pytest.raises(ValueError, match="expected 2 destinations"):
+        hx.ulysses_gather_heads(q, world=2, dst=[FakeDev(bf16(1, 16, 2, 128))])
