@@ -282,3 +282,29 @@ def test_head_chunk_schedule_on_three_streams_matches_one_stream(gpu_lib):
     assert np.array_equal(seq, par)
     # only this rank's band was exchanged: its heads (source 0) are all written
     assert not np.any(seq[:, :, :hl] == O.POISON_BITS)
+
+
+def test_exchange_chunks_at_the_benchmark_message(gpu_lib):
+    """exchange_chunks of the whole-band Q|K|V message of the 56-head U4 shard
+    (B*S_local*H_local*384 bf16 = 101.8 MB per peer, the size the benchmark
+    times), bit for bit; the other senders' slots of every peer keep their
+    fill."""
+    wl = W.WORKLOADS["h56_u4"]
+    U, rank = wl.world, 2
+    msg = wl.batch * wl.s_local * wl.local_heads * 384 * 2
+    assert msg >= 64 << 20
+    g = torch.Generator(device="cuda")
+    g.manual_seed(wl.seed("chunks"))
+    x = torch.randint(0, 256, (U, msg), generator=g, dtype=torch.uint8, device="cuda")
+    outs = [torch.full((U, msg), 0xAB, dtype=torch.uint8, device="cuda") for _ in range(U)]
+    gpu_lib.ulysses_exchange_chunks(x, world=U, rank=rank, dst=outs)
+    torch.cuda.synchronize()
+    xh = x.cpu().numpy()
+    # the oracle over the group, with this rank's payload and fill elsewhere:
+    # a sender whose rows are all 0xAB leaves the fill where it lands
+    fill = np.full((U, msg), 0xAB, np.uint8)
+    ref = O.exchange_chunks([xh if r == rank else fill for r in range(U)], U)
+    for u in range(U):
+        got = outs[u].cpu().numpy()
+        assert np.array_equal(got, ref[u]), f"peer {u}"
+        del got

@@ -4,17 +4,23 @@ Every case compares the receive slots written by the HIP kernel (through the
 C ABI) with the CPU oracle on the same seeded inputs, under the acceptance rule
 of ``helpers.check_fp``.  Small shapes are compared element by element over
 whole slots (several tiles, ragged M and N tails, both layouts, U = 1, odd
-head counts); the five full-size workloads, in the launch configuration the
-benchmark times, are compared on sampled tokens (all heads, all destinations),
-and on the coverage property over the whole slot.
+head counts).  The four full-size multi-head workloads, in the launch
+configuration the benchmark times, are compared element by element over whole
+slots too (every destination, part, head and token; the 48-head stress
+workload on each of its four cycled calls), in token chunks so that the host
+holds one chunk of oracle values at a time; the sampled-token tests are the
+quick form of the same comparison.
 """
+import os
+from concurrent.futures import ThreadPoolExecutor
+
 import numpy as np
 import pytest
 import torch
 
 import oracle as O
 import workloads as W
-from helpers import check_fp, f32_dev, slot_full, slot_rows, to_bits, to_dev
+from helpers import FpCheck, check_fp, f32_dev, slot_full, slot_rows, to_bits, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -337,3 +343,165 @@ def test_largest_group_full(gpu_lib):
     views = run(sess, inp)
     torch.cuda.synchronize()
     check_full(views, inp, wl.rank, "u64")
+
+
+# ---------------------------------------------------------------------------
+# whole slots at full size
+# ---------------------------------------------------------------------------
+
+CHECK_WORKERS = max(1, min(8, os.cpu_count() or 1))
+
+
+def slot_part_bits(view, layout: str, b: int, lo: int, hi: int) -> np.ndarray:
+    """Rows lo..hi-1 of batch entry b of one destination's slot, as
+    [3, rows, H_local, 128] uint16 (q, k, v)."""
+    if layout == "bshd":
+        return np.stack([to_bits(t[b, lo:hi]) for t in view])
+    bits = to_bits(view[b, lo:hi])
+    return np.stack([bits[..., 0:128], bits[..., 128:256], bits[..., 256:384]])
+
+
+def check_coverage(views, wl: W.Workload, rank: int, label: str) -> None:
+    """On the device: every element of this rank's rows was written (no poison
+    left), every other row still holds the poison pattern."""
+    r0, r1 = rank * wl.s_local, (rank + 1) * wl.s_local
+    for d, v in enumerate(views):
+        parts = v if wl.layout == "bshd" else (v,)
+        for t in parts:
+            bits = t.view(torch.int16)
+            assert not bool((bits[:, r0:r1] == int(O.POISON_BITS)).any()), \
+                f"{label}: unwritten element in destination {d}"
+            if r0 > 0:
+                assert bool((bits[:, :r0] == int(O.POISON_BITS)).all()), \
+                    f"{label}: rows before rank {rank} written in destination {d}"
+            if r1 < bits.shape[1]:
+                assert bool((bits[:, r1:] == int(O.POISON_BITS)).all()), \
+                    f"{label}: rows after rank {rank} written in destination {d}"
+
+
+def check_whole_slots(views, inp: Inputs, rank: int, label: str, rope="rotate_half",
+                      chunk: int = 2048) -> list:
+    """Every element of this rank's rows of every destination's slot against
+    the oracle, under the acceptance rule per (destination, part) tensor.
+    The oracle runs on chunks of ``chunk`` tokens of one batch entry; the
+    element-wise checks of a chunk's (destination, part) pieces run in a
+    thread pool (numpy releases the interpreter lock in them)."""
+    wl = inp.wl
+    hl, S = wl.local_heads, wl.s_local
+    x2 = inp.x.reshape(wl.tokens, wl.hidden)
+    r0 = rank * S
+    checks = [[FpCheck(f"{label}:d{d}:{'qkv'[p]}") for p in range(3)] for d in range(wl.world)]
+    with ThreadPoolExecutor(CHECK_WORKERS) as ex:
+        for b in range(wl.batch):
+            for s0 in range(0, S, chunk):
+                s1 = min(s0 + chunk, S)
+                tok = b * S + np.arange(s0, s1)
+                ref = O.front_end_rows(x2[tok], inp.w, inp.wq, inp.wk, inp.cs[r0 + s0:r0 + s1],
+                                       wl.heads, rope)                       # [T, 3, H, 128]
+                got = [slot_part_bits(v, wl.layout, b, r0 + s0, r0 + s1) for v in views]
+                futs = [ex.submit(checks[d][p].add, got[d][p],
+                                  ref[:, p, d * hl:(d + 1) * hl])
+                        for d in range(wl.world) for p in range(3)]
+                for f in futs:
+                    f.result()
+    return [[c.finish() for c in row] for row in checks]
+
+
+@pytest.mark.parametrize("name", ["h32_u4_fused", "h56_u4", "h56_u2_fused"])
+def test_full_size_whole_slots(gpu_lib, name):
+    """The full-size workloads in the launch configuration the benchmark times:
+    all 3108 (56-head U4), 6216 (56-head U2) or 768 (32-head) tiles, claimed
+    across the per-XCD queues; every output element against the oracle."""
+    wl = W.WORKLOADS[name]
+    inp = Inputs(wl)
+    sess = make_session(gpu_lib, wl)
+    sess.poison_receive_slots()
+    views = run(sess, inp)
+    torch.cuda.synchronize()
+    check_coverage(views, wl, wl.rank, name)
+    check_whole_slots(views, inp, wl.rank, name)
+    sess.close()
+
+
+def poison_slot(sess, t: int) -> None:
+    """Fill receive slot t (every destination's region) with the poison
+    pattern, leaving the other slots as they are.  The slot memory is the
+    session's control area followed by num_slots * world regions of
+    max_tokens * 3 * hidden elements, slot-major."""
+    import head_exchange_amd as hx
+    region = sess.max_tokens * 3 * sess.hidden
+    lo = hx.CTRL_BYTES // 2 + t * sess.world * region
+    sess.slots.view(torch.int16)[lo:lo + sess.world * region].fill_(int(O.POISON_BITS))
+
+
+@pytest.mark.parametrize("call", range(4))
+def test_stress_whole_slots_each_call(gpu_lib, call):
+    """The 48-head U8 stress workload: calls 0..call with fresh activations into
+    two cycled slots; the slot about to be reused is poisoned before each call,
+    so a tile that a call fails to write shows as poison instead of an older
+    call's values.  Call ``call`` is compared whole; the previous call's views
+    are still intact (sampled tokens) and share its slot with the call before."""
+    wl = W.WORKLOADS["h48_u8_stress"]
+    w = W.w_qkv(wl)
+    sess = make_session(gpu_lib, wl)
+    history = []
+    for c in range(call + 1):
+        poison_slot(sess, c % wl.num_slots)
+        inp = Inputs(wl, call=c, w_bits=w)
+        views = run(sess, inp)
+        assert sess.outputs_struct().slot == c % wl.num_slots
+        history.append((views, inp))
+    torch.cuda.synchronize()
+    views, inp = history[-1]
+    check_coverage(views, wl, wl.rank, f"stress:call{call}")
+    check_whole_slots(views, inp, wl.rank, f"stress:call{call}")
+    if call >= 1:
+        pviews, pinp = history[-2]
+        check_coverage(pviews, wl, wl.rank, f"stress:call{call - 1}-kept")
+        check_sampled(pviews, pinp, wl.rank, sample_tokens(wl, n=24), f"stress:call{call - 1}-kept")
+    if call >= 2:
+        assert views[0][0].data_ptr() == history[-3][0][0][0].data_ptr()
+    sess.close()
+
+
+@pytest.mark.parametrize("layout", ["bshd", "fused"])
+def test_tiny_forward_then_merge_round_trip(gpu_lib, layout):
+    """The tiny workload chained through the exchange and back: forward stores
+    this rank's Q, K and V into the U receive slots, and merging every chunk of
+    the schedule from those slots (sources at rows rank*S_local.., band heads
+    at the chunk's offset) rebuilds this rank's [B, S_local, H, 128] Q, K and V.
+    The rebuilt tensors equal the slots' contents bit for bit, and the oracle's
+    values under the acceptance rule."""
+    base = W.WORKLOADS["tiny"]
+    wl = W.custom(base.index, name=f"tiny_{layout}", batch=base.batch, s_local=base.s_local,
+                  heads=base.heads, world=base.world, rank=1, layout=layout,
+                  schedule=base.schedule, rope_base=base.rope_base,
+                  cos_sin_rows=base.cos_sin_rows)
+    inp = Inputs(wl)
+    sess = make_session(gpu_lib, wl)
+    sess.poison_receive_slots()
+    views = run(sess, inp)
+    B, S, U, hl, H = wl.batch, wl.s_local, wl.world, wl.local_heads, wl.heads
+    r0 = wl.rank * S
+    merged = []
+    for p in range(3):
+        if layout == "bshd":
+            srcs = [views[u][p] for u in range(U)]
+        else:
+            srcs = [views[u][..., p * 128:(p + 1) * 128] for u in range(U)]
+        out = torch.full((B, S, H, 128), int(O.POISON_BITS), dtype=torch.int16,
+                         device="cuda").view(torch.bfloat16)
+        for chunk, (off, cnt) in enumerate(W.schedule_pairs(wl.schedule)):
+            gpu_lib.ulysses_merge_output_head_chunk(srcs, world=U, local_heads=hl,
+                                                    schedule=wl.schedule, chunk=chunk, out=out,
+                                                    row_offset=r0, head_offset=off)
+        merged.append(out)
+    torch.cuda.synchronize()
+    slots = slot_full(views, layout)                     # [3, B, S_g, hl, 128] per destination
+    vals = O.front_end_values(inp.x, inp.w, inp.wq, inp.wk, inp.cs, H, wl.rank)
+    for p, name in enumerate("qkv"):
+        got = to_bits(merged[p])
+        want = np.concatenate([slots[u][p][:, r0:r0 + S] for u in range(U)], axis=2)
+        assert np.array_equal(got, want), f"{layout}:{name}: merge does not return the slots"
+        check_fp(got, vals[:, :, p], f"round trip {layout}:{name}")
+    sess.close()

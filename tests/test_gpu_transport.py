@@ -90,7 +90,7 @@ def test_pack_chunks_into_whole_band_equal_whole_band_pack(gpu_lib):
         assert np.array_equal(to_bits(parts[d]), to_bits(whole[d]))
 
 
-@pytest.mark.parametrize("name", ["tiny", "h56_u4", "h56_u2_fused"])
+@pytest.mark.parametrize("name", W.ORDER)
 def test_merge_band_form(gpu_lib, name):
     """The attention-output band [B, S_global, H_local, 128]: source u is its
     sequence segment u; every chunk merged into a poisoned output equals the
