@@ -1,11 +1,12 @@
 // The consumer side of the readiness words: a one-wave kernel that waits on a
 // device word, so that work enqueued after it on the same stream starts only
-// once a producer running on another stream has published its stores.  This is
-// the single-GPU form of the pages' wait kernel ("Fused QKV Projection + Norm +
-// RoPE + Head Exchange" on docs.flashinfer.ai/api/comm.html: a one-CTA wait
-// kernel on a consumer stream acquires the readiness words and the caller's
-// stream joins it).  The wait is bounded: after spin_limit polls it gives up,
-// counts a timeout and returns, so the kernel always exits.
+// once a producer running on another stream has published its stores.  On the
+// pages ("Fused QKV Projection + Norm + RoPE + Head Exchange" on
+// docs.flashinfer.ai/api/comm.html) a single small workgroup, launched on a
+// separate stream, does this acquire, and the caller's stream then waits for
+// that stream; this kernel is the one-GPU version of it.  The wait is bounded:
+// after spin_limit polls it gives up, counts a timeout and returns, so the
+// kernel always exits.
 #include "qkvx_internal.h"
 
 namespace qkvx {
