@@ -30,7 +30,7 @@ EXPORTS = ("qkvx_last_error", "qkvx_slot_bytes", "qkvx_create", "qkvx_forward",
            "qkvx_destroy", "ulysses_pack_qkv_head_chunk", "ulysses_merge_output_head_chunk",
            "ulysses_scatter_heads", "ulysses_gather_heads", "ulysses_pack_output_sequence_chunk",
            "ulysses_exchange_chunks", "qkvx_set_publish", "qkvx_wait_ready", "qkvx_wait_word",
-           "qkvx_ready_state", "qkvx_ready_expected")
+           "qkvx_ready_state", "qkvx_ready_expected", "qkvx_forward_noalloc")
 
 
 class QkvxError(RuntimeError):
@@ -90,6 +90,9 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.qkvx_forward.restype = i32
     lib.qkvx_forward.argtypes = [vp, vp, i32, i32, vp, vp, vp, vp, i64, i32, vp,
                                  ctypes.POINTER(Outputs)]
+    lib.qkvx_forward_noalloc.restype = i32
+    lib.qkvx_forward_noalloc.argtypes = [i32, i32, i32, i32, i32, vp, i32, i32, vp, vp, vp, vp,
+                                         i64, i32, vp, sz, vp, ctypes.POINTER(Outputs)]
     lib.qkvx_last_outputs.restype = i32
     lib.qkvx_last_outputs.argtypes = [vp, ctypes.POINTER(Outputs)]
     lib.qkvx_poison_receive_slots.restype = i32
@@ -223,6 +226,24 @@ def _schedule(schedule: Sequence[int]):
 # fused projection session
 # ---------------------------------------------------------------------------
 
+def _output_views(memory, o: Outputs) -> List:
+    """torch views of the receive slot that ``o`` describes, inside ``memory``
+    (a 16-bit device tensor holding it): ``[(q, k, v), ...]`` per destination
+    for bshd, ``[payload, ...]`` for fused."""
+    import torch
+    base = memory.data_ptr()
+    shape = (o.batch, o.s_global, o.local_heads, HEAD_DIM if o.layout == 0 else 3 * HEAD_DIM)
+    stride = tuple(o.stride[i] for i in range(4))
+    out = []
+    flat = memory.view(torch.bfloat16)
+    for d in range(o.world):
+        if o.layout == 0:
+            out.append(tuple(torch.as_strided(flat, shape, stride, (ptr - base) // 2)
+                             for ptr in (o.q[d], o.k[d], o.v[d])))
+        else:
+            out.append(torch.as_strided(flat, shape, stride, (o.q[d] - base) // 2))
+    return out
+
 def qkvx_slot_bytes(hidden: int, world: int, max_tokens: int, num_slots: int = 2) -> int:
     return int(load().qkvx_slot_bytes(hidden, world, max_tokens, num_slots))
 
@@ -263,20 +284,7 @@ class Session:
 
     # -- views ---------------------------------------------------------------
     def _views(self, o: Outputs) -> List:
-        import torch
-        base = self.slots.data_ptr()
-        shape = (o.batch, o.s_global, o.local_heads,
-                 HEAD_DIM if o.layout == 0 else 3 * HEAD_DIM)
-        stride = tuple(o.stride[i] for i in range(4))
-        out = []
-        flat = self.slots.view(torch.bfloat16)
-        for d in range(o.world):
-            if o.layout == 0:
-                out.append(tuple(torch.as_strided(flat, shape, stride, (ptr - base) // 2)
-                                 for ptr in (o.q[d], o.k[d], o.v[d])))
-            else:
-                out.append(torch.as_strided(flat, shape, stride, (o.q[d] - base) // 2))
-        return out
+        return _output_views(self.slots, o)
 
     def forward(self, x, w_qkv, q_norm_w, k_norm_w, cos_sin, rank: int, stream=None):
         """Run one call; returns per-destination views of the receive slot:
@@ -369,6 +377,53 @@ def qkvx_create(hidden: int, num_heads: int, head_dim: int = HEAD_DIM, world: in
 def qkvx_forward(session: Session, x, w_qkv, q_norm_w, k_norm_w, cos_sin, rank: int,
                  stream=None):
     return session.forward(x, w_qkv, q_norm_w, k_norm_w, cos_sin, rank, stream)
+
+
+def noalloc_slot_elems(hidden: int, world: int, tokens: int) -> int:
+    """16-bit elements of the receive slot a qkvx_forward_noalloc call of
+    ``tokens`` = batch * s_local tokens writes: world regions of tokens*3*hidden."""
+    return world * tokens * 3 * hidden
+
+
+def qkvx_forward_noalloc(x, w_qkv, q_norm_w, k_norm_w, cos_sin, rank: int, slot, *,
+                         num_heads: int, world: int, layout: str = "bshd",
+                         rope: str = "rotate_half", stream=None):
+    """The forward call that allocates nothing (``qkvx_forward_noalloc``): the
+    same outputs as a session's forward, written into ``slot``, a caller-owned
+    16-bit device tensor of at least ``noalloc_slot_elems`` elements.  Returns
+    the per-destination views into ``slot``.  Calls on one GPU share the
+    library's scratch array and must not overlap."""
+    _check_bf16(x, "x")
+    _check_bf16(w_qkv, "w_qkv")
+    _check_bf16(slot, "slot")
+    for t, n in ((x, "x"), (w_qkv, "w_qkv"), (slot, "slot")):
+        _on_gpu(t, n)
+    if layout not in LAYOUTS:
+        raise QkvxValueError(-7, f"layout {layout!r} is neither 'bshd' nor 'fused'")
+    if rope not in ROPES:
+        raise QkvxValueError(-1, f"rope {rope!r} is neither 'rotate_half' nor 'interleaved'")
+    hidden = num_heads * HEAD_DIM
+    if x.dim() != 3 or not x.is_contiguous() or x.shape[2] != hidden:
+        raise ValueError(f"x must be a contiguous [B, S_local, {hidden}] tensor, "
+                         f"got {tuple(x.shape)}")
+    if tuple(w_qkv.shape) != (3 * hidden, hidden) or not w_qkv.is_contiguous():
+        raise ValueError(f"w_qkv must be a contiguous [{3 * hidden}, {hidden}] tensor, "
+                         f"got {tuple(w_qkv.shape)}")
+    if not slot.is_contiguous():
+        raise ValueError("slot must be contiguous")
+    _check_f32(q_norm_w, "q_norm_w", 128)
+    _check_f32(k_norm_w, "k_norm_w", 128)
+    _check_f32(cos_sin, "cos_sin", 0)
+    if cos_sin.dim() != 2 or cos_sin.shape[1] != 128:
+        raise ValueError("cos_sin must be a [rows, 128] float32 table")
+    o = Outputs()
+    _check(load().qkvx_forward_noalloc(hidden, num_heads, world, LAYOUTS[layout], ROPES[rope],
+                                       x.data_ptr(), x.shape[0], x.shape[1], w_qkv.data_ptr(),
+                                       q_norm_w.data_ptr(), k_norm_w.data_ptr(),
+                                       cos_sin.data_ptr(), cos_sin.shape[0], rank,
+                                       slot.data_ptr(), slot.numel() * slot.element_size(),
+                                       _stream(stream), ctypes.byref(o)))
+    return _output_views(slot, o)
 
 
 # ---------------------------------------------------------------------------

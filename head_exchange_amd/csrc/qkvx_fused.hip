@@ -57,9 +57,19 @@
 //    lanes of tokens 16 apart trade pieces so that each (nontemporal) store
 //    instruction writes whole 128-byte lines, and an m-block's stores go out
 //    together.
+#include <mutex>
+
 #include "qkvx_internal.h"
 
 namespace qkvx {
+
+// Device scratch of qkvx_forward_noalloc: the tile-claim counters of its
+// launches, in memory the library never allocates.  Every GPU holds its own
+// copy, shared by all such calls on that GPU, for the life of the process.
+// Host code must not take this name for a device address: it uses the
+// per-device address from scratch_address().
+static __device__ __align__(256) unsigned int scratch[kScratchWords];
+
 namespace {
 
 constexpr int BM = 256;        // tokens per tile
@@ -798,6 +808,36 @@ void fused_qkv_kernel(FusedArgs a) {
 }  // namespace
 
 FusedPlan fused_plan() { return FusedPlan{BM, BN, BK, NT, GROUP_M}; }
+
+namespace {
+__global__ __launch_bounds__(64) void clear_words_kernel(unsigned int* p, int n) {
+    for (int i = threadIdx.x; i < n; i += 64) p[i] = 0u;
+}
+}  // namespace
+
+hipError_t scratch_address(unsigned int** out) {
+    static std::mutex mu;
+    static unsigned int* ptr[kMaxDevices] = {};
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(mu);
+    if (!ptr[dev]) {
+        // once per device, with that device current
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        ptr[dev] = static_cast<unsigned int*>(p);
+    }
+    *out = ptr[dev];
+    return hipSuccess;
+}
+
+hipError_t launch_clear_words(unsigned int* p, int n, hipStream_t stream) {
+    hipLaunchKernelGGL(clear_words_kernel, dim3(1), dim3(64), 0, stream, p, n);
+    return hipGetLastError();
+}
 
 // Compute units of the current device (cached per device).
 static int device_cus() {

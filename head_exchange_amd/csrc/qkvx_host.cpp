@@ -143,6 +143,49 @@ Range peers_touched(const qkvx_peers* p, int u, int64_t batch, int64_t s, int he
     return Range{b + uintptr_t(first) * 2, b + uintptr_t(last + 1) * 2};
 }
 
+// Session shape: the checks of qkvx_create that do not depend on the token count.
+int check_shape(int hidden, int num_heads, int head_dim, int world, int layout, int rope) {
+    if (head_dim != QKVX_HEAD_DIM)
+        return fail(QKVX_ERR_INVALID, "head_dim must be %d (got %d)", QKVX_HEAD_DIM, head_dim);
+    if (num_heads <= 0) return fail(QKVX_ERR_INVALID, "num_heads must be > 0");
+    if (hidden != num_heads * head_dim)
+        return fail(QKVX_ERR_INVALID, "hidden %d != num_heads %d * head_dim %d", hidden,
+                    num_heads, head_dim);
+    if (world < 1 || world > QKVX_MAX_WORLD)
+        return fail(QKVX_ERR_INVALID, "world %d outside [1, %d]", world, QKVX_MAX_WORLD);
+    if (num_heads % world)
+        return fail(QKVX_ERR_DIVISIBILITY, "num_heads %d is not divisible by world %d",
+                    num_heads, world);
+    if (layout != QKVX_LAYOUT_BSHD && layout != QKVX_LAYOUT_FUSED)
+        return fail(QKVX_ERR_LAYOUT, "layout %d is neither bshd (0) nor fused (1)", layout);
+    if (rope != QKVX_ROPE_ROTATE_HALF && rope != QKVX_ROPE_INTERLEAVED)
+        return fail(QKVX_ERR_INVALID, "rope %d is neither rotate-half (0) nor interleaved (1)",
+                    rope);
+    // W [3 hidden, hidden]: element extent below 2^31, byte offsets of padded
+    // tiles below 2^32
+    const int64_t w_elems = int64_t(3) * hidden * hidden;
+    if (w_elems >= kInt32Limit || (int64_t(3) * hidden + 256) * hidden * 2 >= kUint32Limit)
+        return fail(QKVX_ERR_INT32_RANGE, "W_qkv [%d, %d] exceeds the 2^31-element limit",
+                    3 * hidden, hidden);
+    return QKVX_OK;
+}
+
+// Token capacity (max_tokens of a session, or the token count of a call without
+// one): x [tokens, hidden] and one receive region of tokens * 3 * hidden
+// elements stay below 2^31 elements, x's padded tiles below 2^32 bytes.
+int check_tokens(int hidden, int64_t tokens, const char* name) {
+    if (tokens < 1) return fail(QKVX_ERR_INVALID, "%s must be >= 1", name);
+    const int64_t x_elems = tokens * hidden;
+    const int64_t region = tokens * 3 * int64_t(hidden);
+    if (x_elems >= kInt32Limit || (tokens + 256) * hidden * 2 >= kUint32Limit)
+        return fail(QKVX_ERR_INT32_RANGE, "%s %lld x hidden %d exceeds the 2^31 limit", name,
+                    (long long)tokens, hidden);
+    if (region >= kInt32Limit)
+        return fail(QKVX_ERR_INT32_RANGE, "a receive region of %lld elements exceeds 2^31",
+                    (long long)region);
+    return QKVX_OK;
+}
+
 }  // namespace
 
 // ===========================================================================
@@ -184,38 +227,12 @@ int qkvx_create(int hidden, int num_heads, int head_dim, int world, int layout, 
                 qkvx_session** out) {
     if (!out) return fail(QKVX_ERR_INVALID, "out is NULL");
     *out = nullptr;
-    if (head_dim != QKVX_HEAD_DIM)
-        return fail(QKVX_ERR_INVALID, "head_dim must be %d (got %d)", QKVX_HEAD_DIM, head_dim);
-    if (num_heads <= 0) return fail(QKVX_ERR_INVALID, "num_heads must be > 0");
-    if (hidden != num_heads * head_dim)
-        return fail(QKVX_ERR_INVALID, "hidden %d != num_heads %d * head_dim %d", hidden,
-                    num_heads, head_dim);
-    if (world < 1 || world > QKVX_MAX_WORLD)
-        return fail(QKVX_ERR_INVALID, "world %d outside [1, %d]", world, QKVX_MAX_WORLD);
-    if (num_heads % world)
-        return fail(QKVX_ERR_DIVISIBILITY, "num_heads %d is not divisible by world %d",
-                    num_heads, world);
-    if (layout != QKVX_LAYOUT_BSHD && layout != QKVX_LAYOUT_FUSED)
-        return fail(QKVX_ERR_LAYOUT, "layout %d is neither bshd (0) nor fused (1)", layout);
-    if (rope != QKVX_ROPE_ROTATE_HALF && rope != QKVX_ROPE_INTERLEAVED)
-        return fail(QKVX_ERR_INVALID, "rope %d is neither rotate-half (0) nor interleaved (1)",
-                    rope);
-    if (max_tokens < 1) return fail(QKVX_ERR_INVALID, "max_tokens must be >= 1");
+    int st = check_shape(hidden, num_heads, head_dim, world, layout, rope);
+    if (st) return st;
     if (num_slots < 1) return fail(QKVX_ERR_INVALID, "num_slots must be >= 1");
-    // operands: x [M, hidden], W [3 hidden, hidden]; byte offsets of padded
-    // tiles stay below 2^32, element extents below 2^31.
-    const int64_t w_elems = int64_t(3) * hidden * hidden;
-    const int64_t x_elems = max_tokens * hidden;
+    st = check_tokens(hidden, max_tokens, "max_tokens");
+    if (st) return st;
     const int64_t region = max_tokens * 3 * int64_t(hidden);
-    if (w_elems >= kInt32Limit || (int64_t(3) * hidden + 256) * hidden * 2 >= kUint32Limit)
-        return fail(QKVX_ERR_INT32_RANGE, "W_qkv [%d, %d] exceeds the 2^31-element limit",
-                    3 * hidden, hidden);
-    if (x_elems >= kInt32Limit || (max_tokens + 256) * hidden * 2 >= kUint32Limit)
-        return fail(QKVX_ERR_INT32_RANGE, "max_tokens %lld x hidden %d exceeds the 2^31 limit",
-                    (long long)max_tokens, hidden);
-    if (region >= kInt32Limit)
-        return fail(QKVX_ERR_INT32_RANGE, "a receive region of %lld elements exceeds 2^31",
-                    (long long)region);
     const size_t need = qkvx_slot_bytes(hidden, world, max_tokens, num_slots);
     bool owns = false;
     if (slot_memory) {
@@ -280,47 +297,59 @@ int qkvx_destroy(qkvx_session* s) {
     return ok();
 }
 
-static void fill_outputs(const qkvx_session* s, int slot, int batch, int s_local, int rank,
-                         qkvx_outputs* o) {
+// Views of one receive slot whose destination regions start region_elems
+// apart at `first` (destination 0).
+static void outputs_at(int heads, int world, int layout, uint16_t* first, int64_t region_elems,
+                       int slot, int batch, int s_local, int rank, qkvx_outputs* o) {
     memset(o, 0, sizeof(*o));
-    const int64_t hl = s->heads / s->world;
-    const int64_t sg = int64_t(s->world) * s_local;
+    const int64_t hl = heads / world;
+    const int64_t sg = int64_t(world) * s_local;
     o->slot = slot;
-    o->world = s->world;
-    o->layout = s->layout;
+    o->world = world;
+    o->layout = layout;
     o->rank = rank;
     o->batch = batch;
     o->s_global = sg;
     o->local_heads = hl;
     o->head_dim = QKVX_HEAD_DIM;
-    const int64_t inner = s->layout == QKVX_LAYOUT_BSHD ? 128 : 384;
+    const int64_t inner = layout == QKVX_LAYOUT_BSHD ? 128 : 384;
     o->stride[3] = 1;
     o->stride[2] = inner;
     o->stride[1] = hl * inner;
     o->stride[0] = sg * hl * inner;
-    const int64_t part = s->layout == QKVX_LAYOUT_BSHD ? batch * sg * hl * 128 : 128;
-    for (int d = 0; d < s->world; ++d) {
-        uint16_t* base = s->slots + (int64_t(slot) * s->world + d) * s->region_elems;
+    const int64_t part = layout == QKVX_LAYOUT_BSHD ? batch * sg * hl * 128 : 128;
+    for (int d = 0; d < world; ++d) {
+        uint16_t* base = first + int64_t(d) * region_elems;
         o->q[d] = base;
         o->k[d] = base + part;
         o->v[d] = base + 2 * part;
     }
 }
 
-int qkvx_forward(qkvx_session* s, const void* x, int batch, int s_local, const void* w_qkv,
-                 const float* q_norm_w, const float* k_norm_w, const float* cos_sin,
-                 int64_t cos_sin_rows, int rank, void* stream, qkvx_outputs* out) {
-    if (!s) return fail(QKVX_ERR_INVALID, "session is NULL");
+static void fill_outputs(const qkvx_session* s, int slot, int batch, int s_local, int rank,
+                         qkvx_outputs* o) {
+    outputs_at(s->heads, s->world, s->layout,
+               s->slots + int64_t(slot) * s->world * s->region_elems, s->region_elems, slot, batch,
+               s_local, rank, o);
+}
+
+// The per-call checks of a forward call (session or not), all before any
+// launch: pointers, token count against the capacity, rank, table, alignment,
+// and no input overlapping the output memory [out_lo, out_hi).
+static int check_call(int hidden, int world, const void* x, int batch, int s_local,
+                      const void* w_qkv, const float* q_norm_w, const float* k_norm_w,
+                      const float* cos_sin, int64_t cos_sin_rows, int rank, int64_t capacity,
+                      const char* capacity_name, Range outputs, const char* outputs_name) {
     if (!x || !w_qkv || !q_norm_w || !k_norm_w || !cos_sin)
         return fail(QKVX_ERR_INVALID, "x, w_qkv, q_norm_w, k_norm_w and cos_sin must be non-NULL");
     if (batch < 1 || s_local < 1)
         return fail(QKVX_ERR_INVALID, "batch %d and s_local %d must be >= 1", batch, s_local);
     const int64_t M = int64_t(batch) * s_local;
-    if (M > s->max_tokens)
-        return fail(QKVX_ERR_CAPACITY, "batch * s_local = %lld exceeds max_tokens %lld",
-                    (long long)M, (long long)s->max_tokens);
-    if (rank < 0 || rank >= s->world)
-        return fail(QKVX_ERR_INVALID, "rank %d outside [0, %d)", rank, s->world);
+    if (M > capacity)
+        return fail(QKVX_ERR_CAPACITY, "batch * s_local = %lld exceeds %s %lld", (long long)M,
+                    capacity_name, (long long)capacity);
+    if (rank < 0 || rank >= world)
+        return fail(QKVX_ERR_INVALID, "rank %d outside [0, %d)", rank, world);
     if (cos_sin_rows < int64_t(rank + 1) * s_local)
         return fail(QKVX_ERR_CAPACITY, "cos_sin has %lld rows, positions up to %lld are needed",
                     (long long)cos_sin_rows, (long long)(int64_t(rank + 1) * s_local));
@@ -331,20 +360,22 @@ int qkvx_forward(qkvx_session* s, const void* x, int batch, int s_local, const v
     if (!aligned16(q_norm_w) || !aligned16(k_norm_w) || !aligned16(cos_sin))
         return fail(QKVX_ERR_ALIGNMENT,
                     "cos_sin and the norm weights must start at 16-byte aligned addresses");
-    const int64_t hidden = s->hidden;
-    const Range slots = bytes_range(s->memory, int64_t(s->slot_bytes));
-    const Range ins[5] = {bytes_range(x, M * hidden * 2), bytes_range(w_qkv, 3 * hidden * hidden * 2),
+    const int64_t h = hidden;
+    const Range ins[5] = {bytes_range(x, M * h * 2), bytes_range(w_qkv, 3 * h * h * 2),
                           bytes_range(q_norm_w, 512), bytes_range(k_norm_w, 512),
                           bytes_range(cos_sin, cos_sin_rows * 512)};
     const char* names[5] = {"x", "w_qkv", "q_norm_w", "k_norm_w", "cos_sin"};
     for (int i = 0; i < 5; ++i)
-        if (overlap(slots, ins[i]))
-            return fail(QKVX_ERR_ALIAS, "%s overlaps the session's receive slots", names[i]);
+        if (overlap(outputs, ins[i]))
+            return fail(QKVX_ERR_ALIAS, "%s overlaps %s", names[i], outputs_name);
+    return QKVX_OK;
+}
 
-    const int slot = int(s->calls % s->num_slots);
-    qkvx_outputs o;
-    fill_outputs(s, slot, batch, s_local, rank, &o);
-
+// Kernel arguments of one forward call writing the slot described by o.
+static FusedArgs fused_args(int hidden, int heads, int world, int rope, const qkvx_outputs& o,
+                            int64_t region_elems, const void* x, int batch, int s_local,
+                            const void* w_qkv, const float* q_norm_w, const float* k_norm_w,
+                            const float* cos_sin, int rank) {
     FusedArgs a;
     memset(&a, 0, sizeof(a));
     a.x = static_cast<const uint16_t*>(x);
@@ -353,20 +384,41 @@ int qkvx_forward(qkvx_session* s, const void* x, int batch, int s_local, const v
     a.wk = k_norm_w;
     a.cs = cos_sin;
     a.slot = static_cast<uint16_t*>(o.q[0]);
-    a.region_elems = s->region_elems;
+    a.region_elems = region_elems;
     a.part_stride = static_cast<uint16_t*>(o.k[0]) - static_cast<uint16_t*>(o.q[0]);
     a.stride_b = o.stride[0];
     a.stride_s = o.stride[1];
     a.stride_h = o.stride[2];
-    a.M = int32_t(M);
+    a.M = int32_t(int64_t(batch) * s_local);
     a.N = int32_t(3 * hidden);
     a.K = int32_t(hidden);
     a.hidden = int32_t(hidden);
-    a.local_heads = s->heads / s->world;
+    a.local_heads = heads / world;
     a.s_local = s_local;
     a.row0 = rank * s_local;
-    a.rope_interleaved = s->rope == QKVX_ROPE_INTERLEAVED;
+    a.rope_interleaved = rope == QKVX_ROPE_INTERLEAVED;
     a.eps = 1e-6f;
+    return a;
+}
+
+int qkvx_forward(qkvx_session* s, const void* x, int batch, int s_local, const void* w_qkv,
+                 const float* q_norm_w, const float* k_norm_w, const float* cos_sin,
+                 int64_t cos_sin_rows, int rank, void* stream, qkvx_outputs* out) {
+    if (!s) return fail(QKVX_ERR_INVALID, "session is NULL");
+    int st = check_call(s->hidden, s->world, x, batch, s_local, w_qkv, q_norm_w, k_norm_w,
+                        cos_sin, cos_sin_rows, rank, s->max_tokens, "max_tokens",
+                        bytes_range(s->memory, int64_t(s->slot_bytes)),
+                        "the session's receive slots");
+    if (st) return st;
+    const int64_t M = int64_t(batch) * s_local;
+    const int64_t hidden = s->hidden;
+
+    const int slot = int(s->calls % s->num_slots);
+    qkvx_outputs o;
+    fill_outputs(s, slot, batch, s_local, rank, &o);
+
+    FusedArgs a = fused_args(s->hidden, s->heads, s->world, s->rope, o, s->region_elems, x, batch,
+                             s_local, w_qkv, q_norm_w, k_norm_w, cos_sin, rank);
     if (s->publish) {
         a.ready = s->ready;
         const int hl = s->heads / s->world;
@@ -385,6 +437,53 @@ int qkvx_forward(qkvx_session* s, const void* x, int batch, int s_local, const v
     }
     s->last = o;
     s->has_last = true;
+    if (out) *out = o;
+    return ok();
+}
+
+int qkvx_forward_noalloc(int hidden, int num_heads, int world, int layout, int rope,
+                         const void* x, int batch, int s_local, const void* w_qkv,
+                         const float* q_norm_w, const float* k_norm_w, const float* cos_sin,
+                         int64_t cos_sin_rows, int rank, void* slot, size_t slot_bytes,
+                         void* stream, qkvx_outputs* out) {
+    int st = check_shape(hidden, num_heads, QKVX_HEAD_DIM, world, layout, rope);
+    if (st) return st;
+    if (!slot) return fail(QKVX_ERR_INVALID, "slot is NULL");
+    if (batch < 1 || s_local < 1)
+        return fail(QKVX_ERR_INVALID, "batch %d and s_local %d must be >= 1", batch, s_local);
+    const int64_t M = int64_t(batch) * s_local;
+    st = check_tokens(hidden, M, "batch * s_local");
+    if (st) return st;
+    const int64_t region = M * 3 * int64_t(hidden);
+    const size_t need = size_t(world) * size_t(region) * 2u;
+    if (slot_bytes < need)
+        return fail(QKVX_ERR_CAPACITY, "slot holds %zu bytes, %zu needed", slot_bytes, need);
+    if (reinterpret_cast<uintptr_t>(slot) & 255u)
+        return fail(QKVX_ERR_ALIGNMENT, "slot is not 256-byte aligned");
+    st = check_call(hidden, world, x, batch, s_local, w_qkv, q_norm_w, k_norm_w, cos_sin,
+                    cos_sin_rows, rank, M, "batch * s_local", bytes_range(slot, int64_t(need)),
+                    "slot");
+    if (st) return st;
+    // the current device's copy of the scratch array; its first lookup on a
+    // device is the set-up step (hipGetSymbolAddress, no allocation)
+    unsigned int* scratch = nullptr;
+    hipError_t e = scratch_address(&scratch);
+    if (e != hipSuccess) return hip_fail(e, "looking up the device scratch array");
+
+    qkvx_outputs o;
+    outputs_at(num_heads, world, layout, static_cast<uint16_t*>(slot), region, 0, batch, s_local,
+               rank, &o);
+    FusedArgs a = fused_args(hidden, num_heads, world, rope, o, region, x, batch, s_local, w_qkv,
+                             q_norm_w, k_norm_w, cos_sin, rank);
+    a.sched = scratch;
+    const hipStream_t hs = static_cast<hipStream_t>(stream);
+    // the tile-claim counters must start at zero: cleared by a kernel on the
+    // same stream (a launch leaves them zero too, but an overlapping call on
+    // the same GPU would not)
+    e = launch_clear_words(scratch, kScratchWords, hs);
+    if (e != hipSuccess) return hip_fail(e, "scratch clear launch");
+    e = launch_fused(a, hs);
+    if (e != hipSuccess) return hip_fail(e, "fused projection launch");
     if (out) *out = o;
     return ok();
 }

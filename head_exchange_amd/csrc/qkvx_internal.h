@@ -129,6 +129,17 @@ struct ChunkArgs {
     uint8_t* dst[QKVX_MAX_WORLD];
 };
 
+// The device scratch of qkvx_forward_noalloc: kScratchWords words (256 bytes)
+// per GPU, of which the fused kernel's tile-claim counters use kSchedWords.
+constexpr int kScratchWords = 64;
+constexpr int kMaxDevices = 64;
+static_assert(kSchedWords <= kScratchWords, "tile-claim counters exceed the scratch array");
+// Address of the current device's copy of the scratch array (looked up once
+// per device with hipGetSymbolAddress, then cached).
+hipError_t scratch_address(unsigned int** out);
+// One wave zeroes n words at p (a kernel, not a memset: callers may capture it).
+hipError_t launch_clear_words(unsigned int* p, int n, hipStream_t stream);
+
 // Launchers (enqueue only; arguments already validated).
 hipError_t launch_fused(const FusedArgs& a, hipStream_t stream);
 hipError_t launch_pack(const PackArgs& a, int world, hipStream_t stream);

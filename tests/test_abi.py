@@ -462,3 +462,46 @@ def test_binding_rejects_wrong_shapes_before_any_call():
                                                   for u in range(2)])
     with pytest.raises(ValueError, match="expected 2 destinations"):
         hx.ulysses_gather_heads(q, world=2, dst=[FakeDev(bf16(1, 16, 2, 128))])
+
+
+def noalloc(lib, hidden=512, heads=4, world=2, layout=0, rope=0, x=FAKE + (1 << 36), batch=1,
+            s_local=32, w=FAKE + (2 << 36), wq=FAKE + (3 << 36), wk=FAKE + (3 << 36) + 512,
+            cs=FAKE + (4 << 36), rows=128, rank=0, slot=FAKE, nbytes=None):
+    if nbytes is None:
+        nbytes = world * batch * s_local * 3 * hidden * 2
+    return lib.qkvx_forward_noalloc(hidden, heads, world, layout, rope, ctypes.c_void_p(x), batch,
+                                    s_local, ctypes.c_void_p(w), ctypes.c_void_p(wq),
+                                    ctypes.c_void_p(wk), ctypes.c_void_p(cs), rows, rank,
+                                    ctypes.c_void_p(slot), nbytes, None, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(heads=3), -1),                       # hidden != heads * 128
+    (dict(hidden=384, heads=3), -2),           # heads % world
+    (dict(world=0), -1),
+    (dict(layout=5), -7),
+    (dict(rope=3), -1),
+    (dict(slot=0), -1),
+    (dict(batch=0), -1),
+    (dict(s_local=0), -1),
+    (dict(nbytes=100), -3),                    # the slot is too small
+    (dict(slot=FAKE + 16), -4),                # not 256-byte aligned
+    (dict(rank=2), -1),
+    (dict(rows=40, rank=1), -3),               # table shorter than (rank+1)*s_local
+    (dict(x=FAKE + 8), -4),
+    (dict(x=FAKE + 1024), -5),                 # x inside the slot
+    (dict(hidden=128 * 64, heads=64, world=1, s_local=1 << 17), -6),   # 2^31-element region
+])
+def test_forward_noalloc_rejects_before_launch(lib, kw, status):
+    assert noalloc(lib, **kw) == status, lib.qkvx_last_error()
+    assert lib.qkvx_last_error()
+
+
+def test_forward_noalloc_reaches_the_launch_without_allocating(lib):
+    """With valid arguments and no device, the first device step is the
+    scratch lookup (or the launch), never an allocation."""
+    status = noalloc(lib)
+    msg = lib.qkvx_last_error().decode()
+    assert status == -9, msg
+    assert "scratch" in msg or "launch" in msg, msg
+    assert "alloc" not in msg, msg
