@@ -49,14 +49,17 @@ def parse():
                    help="target duration of the CPU oracle sample")
     p.add_argument("--skip-sweep", action="store_true",
                    help="do not time the other workloads and the cold-cache launches")
-    p.add_argument("--copy-calibration", action="store_true",
-                   help="also run a plain 1 GiB device copy (counter calibration)")
     return p.parse_args()
 
 
 def source_hash(path: str) -> str:
     with open(path, "rb") as f:
         return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def profile_label(path: str) -> str:
+    """Where a figure read from a committed counter summary comes from."""
+    return f"{os.path.relpath(path, ROOT)} @ kernel source {source_hash(FUSED_SOURCE)}"
 
 
 def read_traffic():
@@ -124,7 +127,22 @@ def cpu_baseline(wl, x, w, wq, wk, cs, qkv_src, band, target_s: float):
     flops = 2.0 * wl.batch * T * N * K
     pack_bytes = sum(2.0 * wl.batch * T * U * cnt * 384 * 2 for _, cnt in sched)
     merge_bytes = sum(2.0 * wl.batch * T * U * cnt * 128 * 2 for _, cnt in sched)
+    model = ""
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    try:
+        usable = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        usable = os.cpu_count() or 1
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "host_cpus": os.cpu_count(), "usable_cpus": usable, "cpu_model": model,
+            "threads_note": "cores = BLAS threads of the float64 projection; the rest of the "
+                            "oracle runs on one thread",
             "fused_tflops": flops / parts["fused"] / 1e12,
             "pack_gbps": pack_bytes / parts["pack"] / 1e9,
             "merge_gbps": merge_bytes / parts["merge"] / 1e9,
@@ -166,19 +184,29 @@ def pct(ms):
             "p90_us": float(np.percentile(a, 90))}
 
 
+def evict_caches(torch, evict):
+    """Read the 1 GiB buffer ``evict`` (more than the 256 MB MALL and the L2s):
+    afterwards the caches hold clean lines of it and none of the next kernel's
+    inputs.  (A write fill would leave dirty lines whose write-back then falls
+    inside the next timed region.)"""
+    return evict.view(torch.int32).sum(dtype=torch.int64)
+
+
 def launch_times(torch, fn, reps: int, stream, lead, evict=None):
     """Per-launch times (ms) from HIP events recorded on the launch stream around
-    each launch.  With ``evict`` (a 1 GiB device buffer) each launch is preceded
-    by a fill of that buffer, so its inputs start outside the MALL and L2s.  A
-    lead fill of ``lead`` queues ahead of the first launch so that the host stays
-    ahead of the device and no enqueue latency falls between a launch's events."""
+    each launch (for kernels of a millisecond or more: a pair of events costs a
+    few microseconds).  With ``evict`` (a 1 GiB device buffer) each launch is
+    preceded by a read of that buffer, so its inputs start outside the MALL and
+    L2s.  A lead fill of ``lead`` queues ahead of the first launch so that the
+    host stays ahead of the device and no enqueue latency falls between a
+    launch's events."""
     fn()
     torch.cuda.synchronize()
     lead.fill_(0)
     evs = []
     for i in range(reps):
         if evict is not None:
-            evict.fill_(i & 0xFF)
+            evict_caches(torch, evict)
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record(stream)
         fn()
@@ -186,6 +214,72 @@ def launch_times(torch, fn, reps: int, stream, lead, evict=None):
         evs.append((e0, e1))
     torch.cuda.synchronize()
     return [a.elapsed_time(b) for a, b in evs]
+
+
+LEAD_CYCLES = 4_000_000       # a spin of about 2 ms queued ahead of timed launches
+
+
+def back_to_back_us(torch, fn, stream, reps: int = 20) -> float:
+    """Mean time of ``fn`` (one or several launches) run ``reps`` times back to
+    back between one pair of events: no per-launch event cost.  A spin kernel
+    queued first (it touches no memory) keeps the device busy while the host
+    enqueues the launches, so that short kernels are not timed at the rate the
+    host issues them (about 12 us per call through the Python binding)."""
+    fn()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda._sleep(LEAD_CYCLES)
+    e0.record(stream)
+    for _ in range(reps):
+        fn()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) * 1e3 / reps
+
+
+def cold_us(torch, fn, stream, evict, reps: int = 10) -> float:
+    """Median time of ``fn`` (one or several launches, between one pair of
+    events) right after a read of the 1 GiB ``evict`` buffer, so that its
+    inputs come from HBM."""
+    fn()
+    torch.cuda.synchronize()
+    out = []
+    for _ in range(reps):
+        evict_caches(torch, evict)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        out.append(e0.elapsed_time(e1) * 1e3)
+    return float(np.median(out))
+
+
+def copy_ceiling(torch, dev, stream, evict):
+    """The practical HBM ceiling: a plain 1 GiB device-to-device copy (torch's
+    copy kernel), back to back and from cold caches; bytes read + written."""
+    import head_exchange_amd as hx
+    src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    src.fill_(1)
+    dst = torch.empty_like(src)
+    nbytes = 2.0 * src.numel()
+    out = {"bytes": nbytes}
+    # torch's copy kernel, and the library's own 16-byte streaming copy (the
+    # exchange_chunks kernel with one peer)
+    cases = {"torch_copy": lambda: dst.copy_(src),
+             "library_copy": lambda: hx.ulysses_exchange_chunks(src.view(1, -1), world=1, rank=0,
+                                                                 dst=[dst.view(1, -1)],
+                                                                 stream=stream)}
+    for name, fn in cases.items():
+        warm = back_to_back_us(torch, fn, stream, 10)
+        cold = cold_us(torch, fn, stream, evict, 5)
+        out[name] = {"warm_us": warm, "warm_gbps": nbytes / (warm * 1e-6) / 1e9,
+                     "warm_frac": nbytes / (warm * 1e-6) / 1e9 / PEAK_HBM_GBPS,
+                     "cold_us": cold, "cold_gbps": nbytes / (cold * 1e-6) / 1e9,
+                     "cold_frac": nbytes / (cold * 1e-6) / 1e9 / PEAK_HBM_GBPS}
+    del src, dst
+    torch.cuda.empty_cache()
+    return out
 
 
 def device_normal(torch, dev, shape, std: float, seed: int):
@@ -198,10 +292,11 @@ def device_normal(torch, dev, shape, std: float, seed: int):
 
 
 def sweep(hx, torch, W, dev, reps: int = 10):
-    """Every multi-head workload at its full size: the fused kernel, and pack and
-    merge per chunk, each timed back to back (warm) and after a 1 GiB eviction
-    fill (cold).  Rates use the algorithmic work: 2*M*N*K for the fused kernel,
-    bytes read + written by the band copy for pack and merge."""
+    """Every multi-head workload at its full size: the fused kernel per launch
+    (warm, and after a read of a 1 GiB buffer: cold), pack and merge per chunk
+    back to back, and the whole schedule of chunks as one group, warm and cold.
+    Rates use the algorithmic work: 2*M*N*K for the fused kernel, bytes read +
+    written by the band copy for pack and merge."""
     stream = torch.cuda.current_stream()
     evict = torch.empty(EVICT_BYTES, dtype=torch.uint8, device=dev)
     out = {}
@@ -257,10 +352,14 @@ def sweep(hx, torch, W, dev, reps: int = 10):
         band = device_normal(torch, dev, (B, wl.s_global, hl, 128), 1.0, wl.seed("band"))
         srcs = [band[:, u * S:(u + 1) * S] for u in range(U)]
         mout = torch.empty(shape, dtype=torch.bfloat16, device=dev)
-        chunks = []
+        # every chunk's destinations stay allocated so that the whole schedule
+        # can run as one group; chunk times are back to back (20 launches
+        # between one pair of events), group times warm and after eviction
+        chunks, fns, dsts = [], {"pack": [], "merge": []}, []
         for c, (off, cnt) in enumerate(sched):
             dst = [torch.empty(B, wl.s_global, cnt, 384, dtype=torch.bfloat16, device=dev)
                    for _ in range(U)]
+            dsts.append(dst)
             cases = {
                 "pack": (lambda c=c, dst=dst: hx.ulysses_pack_qkv_head_chunk(
                     q, k, v, world=U, schedule=wl.schedule, chunk=c, dst=dst,
@@ -271,22 +370,22 @@ def sweep(hx, torch, W, dev, reps: int = 10):
             }
             row = {"heads": cnt}
             for kind, (fn, nbytes) in cases.items():
+                us = back_to_back_us(torch, fn, stream)
                 row[f"{kind}_bytes"] = nbytes
-                for mode, ev in (("warm", None), ("cold", evict)):
-                    st = pct(launch_times(torch, fn, reps, stream, evict, ev))
-                    st["gbps"] = nbytes / (st["median_us"] * 1e-6) / 1e9
-                    st["frac"] = st["gbps"] / PEAK_HBM_GBPS
-                    row[f"{kind}_{mode}"] = st
+                row[f"{kind}_warm_us"] = us
+                row[f"{kind}_warm_frac"] = nbytes / (us * 1e-6) / 1e9 / PEAK_HBM_GBPS
+                fns[kind].append(fn)
             chunks.append(row)
-            del dst
         res["chunks"] = chunks
         for kind in ("pack", "merge"):
-            for mode in ("warm", "cold"):
-                nbytes = sum(r[f"{kind}_bytes"] for r in chunks)
-                us = sum(r[f"{kind}_{mode}"]["median_us"] for r in chunks)
+            nbytes = sum(r[f"{kind}_bytes"] for r in chunks)
+            group = lambda kind=kind: [f() for f in fns[kind]]
+            for mode, us in (("warm", back_to_back_us(torch, group, stream)),
+                             ("cold", cold_us(torch, group, stream, evict))):
                 res[f"{kind}_{mode}_all_chunks"] = {
                     "us": us, "gbps": nbytes / (us * 1e-6) / 1e9,
                     "frac": nbytes / (us * 1e-6) / 1e9 / PEAK_HBM_GBPS}
+        del dsts, fns
         out[name] = res
         del q, k, v, band, srcs, mout
         if wl.pack_source == "fused384":
@@ -333,15 +432,7 @@ def output_side(hx, torch, wl, band, sched, dev, reps: int = 10):
     }
     out = {}
     for name, (fn, nbytes) in cases.items():
-        fn()
-        torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
-        for _ in range(reps):
-            fn()
-        e1.record(stream)
-        torch.cuda.synchronize()
-        us = e0.elapsed_time(e1) * 1e3 / reps
+        us = back_to_back_us(torch, fn, stream, reps)
         gbps = nbytes / (us * 1e-6) / 1e9
         out[name] = {"us": us, "bytes": nbytes, "gbps": gbps, "frac": gbps / PEAK_HBM_GBPS}
     return out
@@ -573,30 +664,16 @@ def main():
     REPS = 20
 
     def amortized_ms(group):
-        group()
-        torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
-        for _ in range(REPS):
-            group()
-        e1.record(stream)
-        torch.cuda.synchronize()
-        return e0.elapsed_time(e1) / REPS
+        return back_to_back_us(torch, group, stream, REPS) * 1e-3
 
     pack_rep_ms, merge_rep_ms = amortized_ms(pack_group), amortized_ms(merge_group)
-
-    calib = None
-    if args.copy_calibration:
-        src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
-        dst = torch.empty_like(src)
-        dst.copy_(src)
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record()
-        dst.copy_(src)
-        e1.record()
-        torch.cuda.synchronize()
-        calib = {"bytes": 2 * (1 << 30), "gbps": 2 * (1 << 30) / (e0.elapsed_time(e1) * 1e-3) / 1e9}
-        del src, dst
+    evict = torch.empty(EVICT_BYTES, dtype=torch.uint8, device=dev)
+    evict.fill_(3)
+    pack_cold_us = cold_us(torch, pack_group, stream, evict)
+    merge_cold_us = cold_us(torch, merge_group, stream, evict)
+    ceiling = copy_ceiling(torch, dev, stream, evict)
+    del evict
+    torch.cuda.empty_cache()
 
     result = {
         "metric": "fused QKV+norm+RoPE+pack TFLOP/s and head-band pack/merge GB/s, 1 GPU",
@@ -632,13 +709,27 @@ def main():
                           "pack_us": pack_rep_ms * 1e3,
                           "pack_frac": pack_bytes / (pack_rep_ms * 1e-3) / 1e9 / PEAK_HBM_GBPS,
                           "merge_us": merge_rep_ms * 1e3,
-                          "merge_frac": merge_bytes / (merge_rep_ms * 1e-3) / 1e9 / PEAK_HBM_GBPS}},
+                          "merge_frac": merge_bytes / (merge_rep_ms * 1e-3) / 1e9 / PEAK_HBM_GBPS},
+                      "cold": {
+                          "note": "each chunk group right after a read of a 1 GiB buffer "
+                                  "(inputs from HBM); median of 10",
+                          "pack_us": pack_cold_us,
+                          "pack_frac": pack_bytes / (pack_cold_us * 1e-6) / 1e9 / PEAK_HBM_GBPS,
+                          "merge_us": merge_cold_us,
+                          "merge_frac": merge_bytes / (merge_cold_us * 1e-6) / 1e9 / PEAK_HBM_GBPS},
+                      "copy_ceiling": ceiling,
+                      "timing_note": "pack_us and merge_us: per-step events around each group "
+                                     "(a pair of events costs a few microseconds); back_to_back: "
+                                     "20 groups between one pair of events"},
         "kernels_ms": {"fused": fused_ms, "pack_all_chunks": pack_ms, "merge_all_chunks": merge_ms},
         "kernels_pct": {n: pct(v) for n, v in per.items()},
     }
+    if traffic is not None:
+        result["roofline"]["traffic_from"] = profile_label(TRAFFIC_FILE)
     counters = read_mfma_counters()
     if counters:
         result["roofline"].update(counters)
+        result["roofline"]["counters_from"] = profile_label(MFMA_FILE)
     result["output_side"] = output_side(hx, torch, wl, band, sched, dev)
     result["readiness"] = readiness(hx, torch, wl, x, w, wq, wk, cs, dev)
     result["head_chunk_pipeline"] = head_chunk_pipeline(hx, torch, wl, q, k, v, sched, dev)
@@ -646,8 +737,6 @@ def main():
         del q, k, v, band, pack_dst, merge_out, merge_src
         torch.cuda.empty_cache()
         result["sweep"] = sweep(hx, torch, W, dev)
-    if calib:
-        result["copy_calibration"] = calib
     if not args.skip_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(wl, x_h, w_h, wq_h, wk_h, cs_h, qkv_h, band_h,
                                               args.cpu_seconds)

@@ -12,12 +12,14 @@
 //   merge  : out[b, s, u*H_local + off + j, e] = src_u[b, R0 + s, j0 + j, e]
 //   scatter: dst_d[b, R0 + s, j0 + j, e] = x[b, s, d*H_local + j, e]
 //   gather : dst_u[b, R0 + s, j0 + j, e] = x[b, u*S_local + s, j, e]
-// The peer index (d or u) is blockIdx.y (pack) or the workgroup index modulo
-// the peer count (band copies), so the peer's base pointers are wave-uniform
-// kernel arguments and no per-lane table lookup is needed; the rest of the flat
-// 16-byte-chunk index is split with precomputed 32-bit dividers.
-// Each thread moves one 16-byte vector with nontemporal accesses (four for
-// small band copies).
+// The peer index (d or u) is blockIdx.y (pack with few peers) or the
+// workgroup index modulo the peer count (band copies, pack with 8 or more
+// peers), so the peer's base pointers are wave-uniform kernel arguments and no
+// per-lane table lookup is needed; the rest of the flat 16-byte-chunk index is
+// split with precomputed 32-bit dividers.
+// Pack moves one 16-byte vector per thread, nontemporal on both sides; the band
+// copies move two per thread, read with the default cache policy and stored
+// nontemporally (see band_copy_kernel).
 #include "qkvx_internal.h"
 
 namespace qkvx {
@@ -37,9 +39,14 @@ __device__ __forceinline__ void store_nt(uint16_t* p, u32x4 v) {
     __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(p));
 }
 
-__global__ __launch_bounds__(kThreads) void pack_kernel(PackArgs a) {
-    const uint32_t d = blockIdx.y;
-    const uint32_t c = blockIdx.x * kThreads + threadIdx.x;
+// PEERS_ALONG_X: the peer is the workgroup index modulo the peer count
+// (workgroups dispatched together read the same tokens' rows for every peer);
+// otherwise blockIdx.y.  Measured on the pages' schedules: along x is 7-10 %
+// faster with 8 peers and 3-4 % slower with 4.
+template <bool PEERS_ALONG_X>
+__global__ __launch_bounds__(kThreads) void pack_kernel(PackArgs a, uint32_t world) {
+    const uint32_t d = PEERS_ALONG_X ? blockIdx.x % world : blockIdx.y;
+    const uint32_t c = (PEERS_ALONG_X ? blockIdx.x / world : blockIdx.x) * kThreads + threadIdx.x;
     // The part's pointer and strides are picked per lane with selects on two
     // flags computed once: the compiler then loads all three parts' arguments
     // up front.  Written as an early return plus nested comparisons it emitted
@@ -67,24 +74,27 @@ __global__ __launch_bounds__(kThreads) void pack_kernel(PackArgs a) {
     if (dst) store_nt(dst, v);
 }
 
-// VPT vectors per thread, kThreads * (workgroups per peer) apart: small copies
-// run with VPT = 4 (a quarter of the workgroups to dispatch, four loads in
-// flight per thread), large ones with VPT = 1, which streams best.  The peers
-// are interleaved along the grid (peer = workgroup % world): workgroups
-// dispatched together cover the same tokens of every peer, so a token's row of
-// the merged output (or of a scatter source) is written (read) in one burst
-// rather than in one pass per peer; measured 6 % faster on the 10-head merge
-// chunk of the 56-head U4 schedule.
-template <int VPT>
+// Two vectors per thread: a workgroup copies 2 * kThreads consecutive vectors
+// of one peer, both loads in flight before the stores.  The peers are
+// interleaved along the grid (peer = workgroup % world): workgroups dispatched
+// together cover the same tokens of every peer, so a token's row of the merged
+// output (or of a scatter source) is written (read) in one burst rather than in
+// one pass per peer (6 % faster on the 10-head merge chunk of the 56-head U4
+// schedule).  The source is read with the default cache policy: a merge's
+// input is the attention output just written, and a band that stays in the
+// 256 MB MALL is served from it, which nontemporal reads do not get (the
+// pages' merge schedules back to back: 41.5 against 47 us on the 56-head U4
+// shard, 83.5 against 96 us on the U2 shard).  From memory that no cache holds
+// both policies run within 10 % of each other.  Stores stay nontemporal.
 __global__ __launch_bounds__(kThreads) void band_copy_kernel(BandCopyArgs a, uint32_t world) {
+    constexpr int VPT = 2;
     const uint32_t y = blockIdx.x % world;
-    const uint32_t step = (gridDim.x / world) * kThreads;
-    const uint32_t c0 = (blockIdx.x / world) * kThreads + threadIdx.x;
+    const uint32_t c0 = (blockIdx.x / world) * (VPT * kThreads) + threadIdx.x;
     u32x4 v[VPT];
     uint16_t* dst[VPT];
 #pragma unroll
     for (int k = 0; k < VPT; ++k) {
-        const uint32_t c = c0 + k * step;
+        const uint32_t c = c0 + k * kThreads;
         dst[k] = nullptr;
         if (c >= a.total) continue;
         const uint32_t e16 = c & 15u;
@@ -92,7 +102,7 @@ __global__ __launch_bounds__(kThreads) void band_copy_kernel(BandCopyArgs a, uin
         a.div_hc.divmod(c >> 4, tok, j);
         a.div_s.divmod(tok, b, s);
         dst[k] = a.dst[y] + b * a.db + s * a.ds + j * a.dh + e16 * 8;
-        v[k] = load_nt(a.src[y] + b * a.sb + s * a.ss + j * a.sh + e16 * 8);
+        v[k] = *reinterpret_cast<const u32x4*>(a.src[y] + b * a.sb + s * a.ss + j * a.sh + e16 * 8);
     }
 #pragma unroll
     for (int k = 0; k < VPT; ++k)
@@ -132,22 +142,20 @@ __global__ __launch_bounds__(kThreads) void fill16_kernel(uint16_t* p, int64_t n
 
 hipError_t launch_pack(const PackArgs& a, int world, hipStream_t stream) {
     if (a.total == 0) return hipSuccess;
-    const uint32_t per_block = kThreads;
-    dim3 grid((a.total + per_block - 1) / per_block, world);
-    hipLaunchKernelGGL(pack_kernel, grid, dim3(kThreads), 0, stream, a);
+    const uint32_t w = uint32_t(world);
+    const uint32_t blocks = (a.total + kThreads - 1) / kThreads;     // per peer
+    if (world >= 8)
+        hipLaunchKernelGGL(pack_kernel<true>, dim3(blocks * w), dim3(kThreads), 0, stream, a, w);
+    else
+        hipLaunchKernelGGL(pack_kernel<false>, dim3(blocks, w), dim3(kThreads), 0, stream, a, w);
     return hipGetLastError();
 }
 
 hipError_t launch_band_copy(const BandCopyArgs& a, int world, hipStream_t stream) {
     if (a.total == 0) return hipSuccess;
     const uint32_t w = uint32_t(world);
-    if (a.total < (1u << 20)) {                       // under 16 MB per peer
-        dim3 grid(((a.total + 4 * kThreads - 1) / (4 * kThreads)) * w);
-        hipLaunchKernelGGL(band_copy_kernel<4>, grid, dim3(kThreads), 0, stream, a, w);
-    } else {
-        dim3 grid(((a.total + kThreads - 1) / kThreads) * w);
-        hipLaunchKernelGGL(band_copy_kernel<1>, grid, dim3(kThreads), 0, stream, a, w);
-    }
+    dim3 grid(((a.total + 2 * kThreads - 1) / (2 * kThreads)) * w);
+    hipLaunchKernelGGL(band_copy_kernel, grid, dim3(kThreads), 0, stream, a, w);
     return hipGetLastError();
 }
 
