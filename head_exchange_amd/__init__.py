@@ -13,7 +13,8 @@ import os
 from typing import List, Optional, Sequence
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(HERE, "libqkvx.so")
+# QKVX_LIB: another build of the same library (the host-sanitized one)
+LIB_PATH = os.environ.get("QKVX_LIB") or os.path.join(HERE, "libqkvx.so")
 HEAD_DIM = 128
 MAX_WORLD = 64
 CTRL_BYTES = 1024       # QKVX_CTRL_BYTES: the session's control area, zeroed at creation
