@@ -482,6 +482,28 @@ def readiness(hx, torch, wl, x, w, wq, wk, cs, dev, reps: int = 5):
             "dest_ready_us": [float(np.mean(r)) for r in ready], "wait_timeouts": timeouts}
 
 
+def reference_gemm(torch, x, w, stream, reps: int = 10):
+    """The vendor library's plain GEMM of the same shape, Y = X W^T in bf16
+    (torch.mm, which calls hipBLASLt; no norm, RoPE or band store), timed per
+    launch like the fused kernel, on the same inputs.  A reference point for the
+    fused kernel's MFMA fraction under the same power limit, not part of the
+    path."""
+    xm = x.view(-1, x.shape[-1])
+    wt = w.t()
+    out = torch.empty(xm.shape[0], w.shape[0], dtype=torch.bfloat16, device=x.device)
+    fn = lambda: torch.mm(xm, wt, out=out)
+    ms = launch_times(torch, fn, reps, stream, out)
+    M, K = xm.shape
+    N = w.shape[0]
+    st = pct(ms)
+    st["tflops"] = 2.0 * M * N * K / (st["median_us"] * 1e-6) / 1e12
+    st["frac"] = st["tflops"] / PEAK_BF16_TFLOPS
+    st["what"] = "torch.mm (hipBLASLt) bf16 GEMM of the same M, N, K; output bf16, no epilogue"
+    del out
+    torch.cuda.empty_cache()
+    return st
+
+
 def head_chunk_pipeline(hx, torch, wl, q, k, v, sched, dev, reps: int = 5):
     """The pages' three-stream head-chunk schedule on one GPU: the input pack
     of chunk N+1, a stand-in consumer of chunk N and the output side of chunk
@@ -730,6 +752,7 @@ def main():
     if counters:
         result["roofline"].update(counters)
         result["roofline"]["counters_from"] = profile_label(MFMA_FILE)
+    result["reference_gemm"] = reference_gemm(torch, x, w, stream)
     result["output_side"] = output_side(hx, torch, wl, band, sched, dev)
     result["readiness"] = readiness(hx, torch, wl, x, w, wq, wk, cs, dev)
     result["head_chunk_pipeline"] = head_chunk_pipeline(hx, torch, wl, q, k, v, sched, dev)
