@@ -575,8 +575,25 @@ def head_chunk_pipeline(hx, torch, wl, q, k, v, sched, dev, reps: int = 5):
         for st in (s_in, s_att):
             main.wait_stream(st)
 
+    def serialized():
+        # the same three streams and the same events, but every stage also waits
+        # for the one before it: the cross-stream hand-offs without any overlap
+        start = torch.cuda.Event()
+        start.record(main)
+        s_in.wait_event(start)
+        last = None
+        for i in range(len(sched)):
+            for st, stage in ((s_in, stage_in), (s_att, stage_att), (s_out, stage_out)):
+                if last is not None:
+                    st.wait_event(last)
+                stage(i, st)
+                last = torch.cuda.Event()
+                last.record(st)
+        main.wait_event(last)
+
     res = {}
-    for name, fn in (("sequential_us", sequential), ("pipelined_us", pipelined)):
+    for name, fn in (("sequential_us", sequential), ("pipelined_us", pipelined),
+                     ("three_streams_serialized_us", serialized)):
         fn()
         torch.cuda.synchronize()
         e0, e1 = ev(), ev()
@@ -587,6 +604,8 @@ def head_chunk_pipeline(hx, torch, wl, q, k, v, sched, dev, reps: int = 5):
         torch.cuda.synchronize()
         res[name] = e0.elapsed_time(e1) * 1e3 / reps
     res["speedup"] = res["sequential_us"] / res["pipelined_us"]
+    res["note"] = ("three_streams_serialized: the three streams with every stage waiting for the "
+                   "previous one (cross-stream hand-offs, no overlap)")
     res["consumer"] = "bf16 matmul of the q band by a [hc*128, hc*128] weight (stand-in)"
     return res
 
