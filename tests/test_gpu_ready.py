@@ -15,8 +15,8 @@ import torch
 import oracle as O
 import workloads as W
 from helpers import check_fp, to_bits
-from test_gpu_fused import (SMALL, Inputs, check_full, check_sampled, make_session, run,
-                            sample_tokens)
+from test_gpu_fused import (SMALL, Inputs, check_coverage, check_full, check_whole_slots,
+                            make_session, run, sample_tokens)
 
 pytestmark = pytest.mark.gpu
 
@@ -54,14 +54,20 @@ def test_words_accumulate_over_calls(gpu_lib):
     assert sess.ready_state()[0] == [per_call * 3] * wl.world
 
 
-def test_full_size_publishing_sampled(gpu_lib):
+def test_full_size_publishing_whole_slots(gpu_lib):
+    """The publishing launch at full size (destination-major tile order over
+    248 compute units, claimed per XCD): every element of every destination's
+    slot against the oracle, the other ranks' rows untouched, and the words at
+    their expected values."""
     wl = W.WORKLOADS["h56_u4"]
     inp = Inputs(wl)
     sess = make_session(gpu_lib, wl)
     sess.set_publish(True)
+    sess.poison_receive_slots()
     views = run(sess, inp)
     torch.cuda.synchronize()
-    check_sampled(views, inp, wl.rank, sample_tokens(wl, n=24), "h56_u4:publish")
+    check_coverage(views, wl, wl.rank, "h56_u4:publish")
+    check_whole_slots(views, inp, wl.rank, "h56_u4:publish")
     assert sess.ready_state() == (sess.ready_expected(), 0)
 
 
