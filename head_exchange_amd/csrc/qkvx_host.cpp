@@ -667,6 +667,20 @@ int ulysses_pack_qkv_head_chunk(const qkvx_view4* q, const qkvx_view4* k, const 
     a.local_heads = hl;
     a.div_hc = FastDiv(uint32_t(hc));
     a.div_s = FastDiv(uint32_t(S));
+    {
+        // bytes the three views span: the sum of their ranges, or the span of
+        // their union when that is smaller (views into one tensor)
+        uintptr_t lo = UINTPTR_MAX, hi = 0;
+        uint64_t sum = 0;
+        for (int i = 0; i < 3; ++i) {
+            const Range r = view_range(parts[i]->base, parts[i]->shape, parts[i]->stride, 4);
+            lo = r.lo < lo ? r.lo : lo;
+            hi = r.hi > hi ? r.hi : hi;
+            sum += uint64_t(r.hi - r.lo);
+        }
+        const uint64_t joint = uint64_t(hi - lo);
+        a.source_bytes = sum < joint ? sum : joint;
+    }
     for (int u = 0; u < world; ++u)
         a.dst[u] = static_cast<uint16_t*>(dst->base[u]) + dst->row_offset * dst->stride[1] +
                    dst->head_offset * dst->stride[2];

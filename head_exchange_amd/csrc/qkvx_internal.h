@@ -104,6 +104,7 @@ struct PackArgs {
     uint32_t total;                // 16-byte chunks per destination
     int32_t local_heads;
     FastDiv div_hc, div_s;
+    uint64_t source_bytes;         // bytes spanned by q, k and v together (launch choice)
     uint16_t* dst[QKVX_MAX_WORLD]; // peer d at [0, row_offset, head_offset, 0]
 };
 

@@ -17,15 +17,18 @@
 // peers), so the peer's base pointers are wave-uniform kernel arguments and no
 // per-lane table lookup is needed; the rest of the flat 16-byte-chunk index is
 // split with precomputed 32-bit dividers.
-// Pack moves one 16-byte vector per thread, nontemporal on both sides; the band
-// copies move two per thread, read with the default cache policy and stored
-// nontemporally (see band_copy_kernel).
+// Vectors per thread and the read cache policy of pack and the band copies are
+// set by measurement (see pack_kernel and band_copy_kernel); every store is
+// nontemporal.
 #include "qkvx_internal.h"
 
 namespace qkvx {
 namespace {
 
 constexpr int kThreads = 256;
+// Sources of a pack at most this large (half the 256 MB MALL) are taken to be
+// cache-resident and read with the default policy.
+constexpr uint64_t kResidentBytes = 128ull << 20;
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 // One 16-byte vector per thread, nontemporal on both sides: the data is used
@@ -39,22 +42,38 @@ __device__ __forceinline__ void store_nt(uint16_t* p, u32x4 v) {
     __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(p));
 }
 
-// PEERS_ALONG_X: the peer is the workgroup index modulo the peer count
-// (workgroups dispatched together read the same tokens' rows for every peer);
-// otherwise blockIdx.y.  Measured on the pages' schedules: along x is 7-10 %
-// faster with 8 peers and 3-4 % slower with 4.
-template <bool PEERS_ALONG_X>
+// Three forms, chosen at launch (measured on the pages' schedules, back to back):
+//  * RESIDENT (sources of at most kResidentBytes, fewer than 8 peers): two
+//    vectors per thread from a block of 2 * kThreads consecutive vectors of
+//    one peer, read with the default cache policy, so sources that still sit
+//    in the 256 MB MALL are served from it (the 32-head shard's q, k, v:
+//    100 MB; its schedule 44.4 -> 34.1 us).  On the larger 56-head sources
+//    this form is 8 % slower than the next one;
+//  * fewer than 8 peers otherwise: one vector per thread, nontemporal reads,
+//    the peer is blockIdx.y;
+//  * 8 or more peers: the peer is the workgroup index modulo the peer count
+//    (workgroups dispatched together read the same tokens' rows for every
+//    peer), one vector per thread, nontemporal reads (48-head U8 schedule
+//    236 -> 212 us; with 4 peers this form is 3-4 % slower).
+// Stores are nontemporal in all three.
+template <bool PEERS_ALONG_X, bool RESIDENT>
 __global__ __launch_bounds__(kThreads) void pack_kernel(PackArgs a, uint32_t world) {
+    constexpr int VPT = RESIDENT ? 2 : 1;
     const uint32_t d = PEERS_ALONG_X ? blockIdx.x % world : blockIdx.y;
-    const uint32_t c = (PEERS_ALONG_X ? blockIdx.x / world : blockIdx.x) * kThreads + threadIdx.x;
+    const uint32_t c0 = (PEERS_ALONG_X ? blockIdx.x / world : blockIdx.x) * (VPT * kThreads) +
+                        threadIdx.x;
     // The part's pointer and strides are picked per lane with selects on two
     // flags computed once: the compiler then loads all three parts' arguments
     // up front.  Written as an early return plus nested comparisons it emitted
     // a branch per part, each with its own scalar load and wait, which measured
     // 5 % slower on the 56-head U4 schedule.
-    u32x4 v;
-    uint16_t* dst = nullptr;
-    if (c < a.total) {
+    u32x4 v[VPT];
+    uint16_t* dst[VPT];
+#pragma unroll
+    for (int k = 0; k < VPT; ++k) {
+        const uint32_t c = c0 + k * kThreads;
+        dst[k] = nullptr;
+        if (c >= a.total) continue;
         const uint32_t e16 = c & 15u;
         uint32_t u = c >> 4;
         const uint32_t p = u % 3u;                 // q, k, v interleaved per head
@@ -68,10 +87,12 @@ __global__ __launch_bounds__(kThreads) void pack_kernel(PackArgs a, uint32_t wor
         const int64_t ss = p0 ? a.ss[0] : (p1 ? a.ss[1] : a.ss[2]);
         const int64_t sh = p0 ? a.sh[0] : (p1 ? a.sh[1] : a.sh[2]);
         src += b * sb + s * ss + int64_t(d * a.local_heads + j) * sh + e16 * 8;
-        dst = a.dst[d] + b * a.db + s * a.ds + j * a.dh + p * 128 + e16 * 8;
-        v = load_nt(src);
+        dst[k] = a.dst[d] + b * a.db + s * a.ds + j * a.dh + p * 128 + e16 * 8;
+        v[k] = RESIDENT ? *reinterpret_cast<const u32x4*>(src) : load_nt(src);
     }
-    if (dst) store_nt(dst, v);
+#pragma unroll
+    for (int k = 0; k < VPT; ++k)
+        if (dst[k]) store_nt(dst[k], v[k]);
 }
 
 // Two vectors per thread: a workgroup copies 2 * kThreads consecutive vectors
@@ -143,11 +164,19 @@ __global__ __launch_bounds__(kThreads) void fill16_kernel(uint16_t* p, int64_t n
 hipError_t launch_pack(const PackArgs& a, int world, hipStream_t stream) {
     if (a.total == 0) return hipSuccess;
     const uint32_t w = uint32_t(world);
-    const uint32_t blocks = (a.total + kThreads - 1) / kThreads;     // per peer
-    if (world >= 8)
-        hipLaunchKernelGGL(pack_kernel<true>, dim3(blocks * w), dim3(kThreads), 0, stream, a, w);
-    else
-        hipLaunchKernelGGL(pack_kernel<false>, dim3(blocks, w), dim3(kThreads), 0, stream, a, w);
+    if (world >= 8) {
+        const uint32_t blocks = (a.total + kThreads - 1) / kThreads;            // per peer
+        hipLaunchKernelGGL((pack_kernel<true, false>), dim3(blocks * w), dim3(kThreads), 0,
+                           stream, a, w);
+    } else if (a.source_bytes <= kResidentBytes) {
+        const uint32_t blocks = (a.total + 2 * kThreads - 1) / (2 * kThreads);  // per peer
+        hipLaunchKernelGGL((pack_kernel<false, true>), dim3(blocks, w), dim3(kThreads), 0,
+                           stream, a, w);
+    } else {
+        const uint32_t blocks = (a.total + kThreads - 1) / kThreads;            // per peer
+        hipLaunchKernelGGL((pack_kernel<false, false>), dim3(blocks, w), dim3(kThreads), 0,
+                           stream, a, w);
+    }
     return hipGetLastError();
 }
 
