@@ -192,6 +192,26 @@ def evict_caches(torch, evict):
     return evict.view(torch.int32).sum(dtype=torch.int64)
 
 
+WARMUP_S = 0.05                # device time of warm-up launches before a timed series
+
+
+def warm_up(torch, fn, seconds: float = WARMUP_S) -> None:
+    """Run ``fn`` back to back for about ``seconds`` so that the clocks settle
+    at the steady state of this load (after an idle gap the first milliseconds
+    run at another clock than the rest: a 0.37 ms kernel timed right away
+    measured 20 % slower than later in the same process)."""
+    fn()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(3):
+        fn()
+    torch.cuda.synchronize()
+    per = max((time.perf_counter() - t0) / 3, 1e-5)
+    for _ in range(int(seconds / per)):
+        fn()
+    torch.cuda.synchronize()
+
+
 def launch_times(torch, fn, reps: int, stream, lead, evict=None):
     """Per-launch times (ms) from HIP events recorded on the launch stream around
     each launch (for kernels of a millisecond or more: a pair of events costs a
@@ -200,8 +220,7 @@ def launch_times(torch, fn, reps: int, stream, lead, evict=None):
     L2s.  A lead fill of ``lead`` queues ahead of the first launch so that the
     host stays ahead of the device and no enqueue latency falls between a
     launch's events."""
-    fn()
-    torch.cuda.synchronize()
+    warm_up(torch, fn)
     lead.fill_(0)
     evs = []
     for i in range(reps):
