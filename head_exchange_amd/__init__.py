@@ -271,11 +271,6 @@ class Session:
         device = torch.device("cuda") if device is None else torch.device(device)
         # 256-byte alignment: torch's allocator returns 512-byte aligned blocks
         self.slots = torch.empty(max(nbytes // 2, 1), dtype=torch.uint16, device=device)
-        if nbytes:
-            # the library needs its control area zero at creation (session
-            # setup: the fill is waited for here, once)
-            self.slots[:CTRL_BYTES // 2].zero_()
-            torch.cuda.synchronize(device)
         h = ctypes.c_void_p()
         _check(lib.qkvx_create(hidden, num_heads, head_dim, world, LAYOUTS[layout], ROPES[rope],
                                max_tokens, num_slots, self.slots.data_ptr(), nbytes,

@@ -200,6 +200,8 @@ struct qkvx_session {
     uint16_t* slots;            // memory + QKVX_CTRL_BYTES
     size_t slot_bytes;          // bytes of memory
     bool owns_slots;
+    bool ctrl_zero;                    // the control area is known to be zero (set by create
+                                       // when it allocates, else by the first forward's clear)
     bool publish;                      // forward calls publish readiness words
     bool last_published;               // the last call did
     // device words in the control area (zero at creation)
@@ -266,6 +268,7 @@ int qkvx_create(int hidden, int num_heads, int head_dim, int world, int layout, 
     s->slots = reinterpret_cast<uint16_t*>(s->memory + QKVX_CTRL_BYTES);
     s->slot_bytes = slot_bytes;
     s->owns_slots = owns;
+    s->ctrl_zero = owns;
     s->calls = 0;
     s->has_last = false;
     s->publish = false;
@@ -425,10 +428,19 @@ int qkvx_forward(qkvx_session* s, const void* x, int batch, int s_local, const v
         a.dest_cols = (hl % 2 == 0 && hidden % 256 == 0) ? hl / 2 : 0;
         a.part_cols = int32_t(hidden / 256);
     }
-    // zero since the session was created; every launch leaves them zero again
+    // zero from creation (or from the clear below) on: every launch leaves them zero again
     a.sched = s->sched;
-    hipError_t e = launch_fused(a, static_cast<hipStream_t>(stream));
+    hipError_t e = hipSuccess;
+    if (!s->ctrl_zero) {
+        // caller-provided memory: the first call clears the control area with a
+        // kernel on its own stream (no allocation, no synchronisation)
+        e = launch_clear_words(reinterpret_cast<unsigned int*>(s->memory), QKVX_CTRL_BYTES / 4,
+                               static_cast<hipStream_t>(stream));
+        if (e != hipSuccess) return hip_fail(e, "control area clear launch");
+    }
+    e = launch_fused(a, static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return hip_fail(e, "fused projection launch");
+    s->ctrl_zero = true;
     s->calls += 1;
     s->last_published = s->publish;
     if (s->publish) {
