@@ -505,3 +505,44 @@ def test_tiny_forward_then_merge_round_trip(gpu_lib, layout):
         assert np.array_equal(got, want), f"{layout}:{name}: merge does not return the slots"
         check_fp(got, vals[:, :, p], f"round trip {layout}:{name}")
     sess.close()
+
+
+def test_largest_call_at_the_int32_limit(gpu_lib):
+    """The largest call the 56-head width takes: M = 99864 tokens, so that one
+    destination's receive region (M * 3 * hidden elements) is just under 2^31,
+    at the last rank of four (the largest row offsets of the slots), fused
+    layout.  x and W are seeded random draws made on the device with torch's
+    generator (too large to draw on the host) and read back for the oracle;
+    sampled tokens (both ends, the last tile row, random ones) are compared
+    with the oracle, and every row of every slot is checked for coverage."""
+    hx = gpu_lib
+    heads, world, rank = 56, 4, 3
+    hidden = heads * 128
+    M = (2 ** 31 - 1) // (3 * hidden)
+    assert M * 3 * hidden < 2 ** 31 <= (M + 1) * 3 * hidden
+    wl = W.custom(70, batch=1, s_local=M, heads=heads, world=world, rank=rank, layout="fused",
+                  schedule=(heads // world,), rope_base=1e6)
+    g = torch.Generator(device="cuda")
+    g.manual_seed(wl.seed("x"))
+    x = torch.randn(1, M, hidden, generator=g, device="cuda").to(torch.bfloat16)
+    g.manual_seed(wl.seed("w"))
+    w = (torch.randn(3 * hidden, hidden, generator=g, device="cuda") * hidden ** -0.5).to(
+        torch.bfloat16)
+    torch.cuda.empty_cache()
+    wq, wk = W.norm_weights(wl)
+    cs = W.table(wl)                                  # [world * M, 128]
+    sess = hx.qkvx_create(hidden, heads, 128, world, "fused", M, 1)
+    sess.poison_receive_slots()
+    views = sess.forward(x, w, f32_dev(wq), f32_dev(wk), f32_dev(cs), rank)
+    torch.cuda.synchronize()
+    check_coverage(views, wl, rank, "int32 limit")
+    tokens = sample_tokens(wl, n=24)
+    tokens = np.unique(np.concatenate([tokens, np.arange(M - 260, M, 37)]))
+    got = slot_rows(views, "fused", np.zeros_like(tokens), rank * M + tokens)
+    xi = torch.as_tensor(tokens, device="cuda", dtype=torch.long)
+    x_rows = to_bits(x[0, xi])
+    w_bits = to_bits(w)
+    ref = O.front_end_rows(x_rows, w_bits, wq, wk, cs[rank * M + tokens], heads)
+    for p, name in enumerate("qkv"):
+        check_fp(got[:, p], ref[:, p], f"int32 limit:{name}")
+    sess.close()
