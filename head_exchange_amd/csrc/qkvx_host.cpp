@@ -338,7 +338,7 @@ static void fill_outputs(const qkvx_session* s, int slot, int batch, int s_local
 
 // The per-call checks of a forward call (session or not), all before any
 // launch: pointers, token count against the capacity, rank, table, alignment,
-// and no input overlapping the output memory [out_lo, out_hi).
+// and no input overlapping the output memory `outputs`.
 static int check_call(int hidden, int world, const void* x, int batch, int s_local,
                       const void* w_qkv, const float* q_norm_w, const float* k_norm_w,
                       const float* cos_sin, int64_t cos_sin_rows, int rank, int64_t capacity,
