@@ -501,6 +501,72 @@ def readiness(hx, torch, wl, x, w, wq, wk, cs, dev, reps: int = 5):
             "dest_ready_us": [float(np.mean(r)) for r in ready], "wait_timeouts": timeouts}
 
 
+def power_sample(torch, fn, seconds: float = 3.0, settle: float = 1.0):
+    """Socket power and per-XCD shader clocks while ``fn`` runs back to back for
+    about ``seconds``: ``amd-smi metric -p -c --csv`` polled from a thread (a
+    child process per poll, 5 s limit each), keeping the polls that start after
+    ``settle`` seconds (the power reading is an average that takes about a
+    second to reach the steady state of a load).  Medians over the kept polls;
+    None when the tool is missing or reports nothing."""
+    import csv
+    import io
+    import shutil
+    import statistics
+    import subprocess
+    import threading
+    tool = shutil.which("amd-smi")
+    if tool is None:
+        return None
+    rows, stop = [], threading.Event()
+
+    def poll():
+        while not stop.is_set():
+            started = time.perf_counter() - t0
+            try:
+                r = subprocess.run([tool, "metric", "-p", "-c", "--csv"], capture_output=True,
+                                   text=True, timeout=5)
+            except (OSError, subprocess.SubprocessError):
+                return
+            if started >= settle:
+                rows.append(r.stdout)
+            stop.wait(0.2)
+
+    warm_up(torch, fn)
+    t0 = time.perf_counter()
+    t = threading.Thread(target=poll)
+    t.start()
+    while time.perf_counter() - t0 < seconds:
+        for _ in range(10):
+            fn()
+        torch.cuda.synchronize()
+    stop.set()
+    t.join()
+    vals = {}
+    for text in rows:
+        table = list(csv.reader(io.StringIO(text.strip())))
+        if len(table) < 2:
+            continue
+        for h, v in zip(table[0], table[1]):
+            keep = (h == "socket_power") or (h.startswith("gfx_") and h.endswith("_clk")
+                                             and "min" not in h and "max" not in h)
+            if keep:
+                try:
+                    vals.setdefault(h, []).append(float(v))
+                except ValueError:
+                    pass
+    if not vals:
+        return None
+    clocks = [statistics.median(v) for h, v in sorted(vals.items()) if h.startswith("gfx_")]
+    out = {"polls": len(rows), "tool": "amd-smi metric -p -c",
+           "window_s": [settle, seconds]}
+    if "socket_power" in vals:
+        out["socket_power_w"] = statistics.median(vals["socket_power"])
+    if clocks:
+        out["xcd_clock_mhz"] = clocks
+        out["xcd_clock_mhz_mean"] = statistics.mean(clocks)
+    return out
+
+
 def reference_gemm(torch, x, w, stream, reps: int = 10):
     """The vendor library's plain GEMM of the same shape, Y = X W^T in bf16
     (torch.mm, which calls hipBLASLt; no norm, RoPE or band store), timed per
@@ -791,6 +857,14 @@ def main():
         result["roofline"].update(counters)
         result["roofline"]["counters_from"] = profile_label(MFMA_FILE)
     result["reference_gemm"] = reference_gemm(torch, x, w, stream)
+    xm, wt = x.view(-1, x.shape[-1]), w.t()
+    for key, fn in (("power_under_fused_kernel",
+                     lambda: sess.forward(x, w, wq, wk, cs, wl.rank, stream)),
+                    ("power_under_reference_gemm", lambda: torch.mm(xm, wt))):
+        try:
+            result[key] = power_sample(torch, fn)
+        except Exception as exc:          # the samples are context; never fail the bench on them
+            result[key] = {"error": str(exc)[:200]}
     result["output_side"] = output_side(hx, torch, wl, band, sched, dev)
     result["readiness"] = readiness(hx, torch, wl, x, w, wq, wk, cs, dev)
     result["head_chunk_pipeline"] = head_chunk_pipeline(hx, torch, wl, q, k, v, sched, dev)
