@@ -362,12 +362,12 @@ void fused_qkv_kernel(FusedArgs a) {
 
     // Load instruction i (0..7) of the W or X half of K-step kidx of the
     // stream (kidx >= KT: the next output tile) into buffer buf.
-    auto load_one = [&](bool is_w, int i, int kidx, int buf) {
+    auto load_one = [&](bool is_w, int i, int kidx, uint32_t buf_addr) {
         const bool nx = kidx >= KT;
         const uint32_t g0 = is_w ? (nx ? gw_nxt : gw_cur) : (nx ? gx_nxt : gx_cur);
         const uint32_t kb = uint32_t(nx ? kidx - KT : kidx) * BK * 2u;
         const uint32_t roff = uint32_t(32 * i) * rowbytes;
-        lds_uint4* dst = ring3 + buf * BUF_CHUNKS + (4 * i + wv) * 64;
+        lds_uint4* dst = (lds_uint4*)(size_t)(buf_addr + uint32_t((4 * i + wv) * 1024));
         // The buffer's range check covers the VGPR offset but not the SGPR
         // offset.  When rows past M are read (ROWS_CHECKED) the row goes into
         // the VGPR offset so that they read as zeros; otherwise every row read
@@ -399,18 +399,23 @@ void fused_qkv_kernel(FusedArgs a) {
     // kt+2, which stays in flight) and for the reads, then the barrier.  A
     // tile's first step has no phase 0: its sub-step-0 fragments are read up
     // front and phase 1 starts the accumulators.
+    // pw: the buffer of the current step's W half.  The LDS byte addresses a
+    // step uses (its W and X buffers, phase 0's fragment-read bases, and the
+    // buffers its loads fill: lx for the X half of kt + 1, lw for the W half of
+    // kt + 2) are carried from the step before, which computes them ahead of
+    // its closing barrier: with one wave per SIMD, address arithmetic after the
+    // barrier would hold back the step's first MFMAs (20 scalar instructions
+    // there measured 1.3-1.7 % of the kernel).
     int pw = 0;
+    auto buf_addr = [&](int b) { return ring0 + uint32_t(b) * (BUF_CHUNKS * 16); };
+    uint32_t wb = buf_addr(0), xb = buf_addr(1), lx = buf_addr(3), lw = buf_addr(4);
+    uint32_t wa0 = wb + wl[0], xa0 = xb + xl[0];
     auto step = [&](int kt, bool first_of_tile) __attribute__((always_inline)) {
-        const int px = pw == 4 ? 0 : pw + 1;
-        const int bx1 = pw >= 2 ? pw - 2 : pw + 3;       // (pw + 3) % 5
-        const int bw2 = pw >= 1 ? pw - 1 : 4;            // (pw + 4) % 5
-        const uint32_t wb = ring0 + uint32_t(pw) * (BUF_CHUNKS * 16);
-        const uint32_t xb = ring0 + uint32_t(px) * (BUF_CHUNKS * 16);
         // phase ph multiplies X set ph ^ 1 (phase 0: the previous K-step's
         // sub-step 1, set 1; phase 1: sub-step 0, set 0) and reads sub-step ph
         // into X set ph
         auto phase = [&](const int ph, const bool init) __attribute__((always_inline)) {
-            const uint32_t wa = wb + wl[ph], xa = xb + xl[ph];
+            const uint32_t wa = ph ? wb + wl[1] : wa0, xa = ph ? xb + xl[1] : xa0;
 #pragma unroll
             for (int nb = 0; nb < 8; ++nb) {
 #pragma unroll
@@ -436,8 +441,8 @@ void fused_qkv_kernel(FusedArgs a) {
                     if (mb == 7 && nb < 7) lds_read(fa[nb], wa, nb);
                     if (mb == 5 || (init && mb == 1)) {
                         const int v = init ? (nb * 2 + (mb == 5 ? 1 : 0)) : (ph * 8 + nb);
-                        if (v < HLOADS) load_one(false, v, kt + 1, bx1);
-                        else load_one(true, v - HLOADS, kt + 2, bw2);
+                        if (v < HLOADS) load_one(false, v, kt + 1, lx);
+                        else load_one(true, v - HLOADS, kt + 2, lw);
                     }
                 }
             }
@@ -445,21 +450,37 @@ void fused_qkv_kernel(FusedArgs a) {
         if (first_of_tile) {
             // sub-step 0 in the order a phase reads it (W block 7 into the
             // buffer phase 1 multiplies)
-            lds_read(w7[0], wb + wl[0], 7);
+            lds_read(w7[0], wa0, 7);
 #pragma unroll
-            for (int k = 0; k < 4; ++k) lds_read(fb[0][k], xb + xl[0], k);
-            lds_read(fa[0], wb + wl[0], 0);
+            for (int k = 0; k < 4; ++k) lds_read(fb[0][k], xa0, k);
+            lds_read(fa[0], wa0, 0);
 #pragma unroll
-            for (int k = 4; k < 8; ++k) lds_read(fb[0][k], xb + xl[0], k);
+            for (int k = 4; k < 8; ++k) lds_read(fb[0][k], xa0, k);
 #pragma unroll
-            for (int k = 1; k < 7; ++k) lds_read(fa[k], wb + wl[0], k);
+            for (int k = 1; k < 7; ++k) lds_read(fa[k], wa0, k);
             phase(1, true);
         } else {
             phase(0, false);
             phase(1, false);
         }
-        asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(HLOADS) : "memory");
-        pw = pw >= 3 ? pw - 3 : pw + 2;                  // (pw + 2) % 5
+        // The next step's buffer addresses are computed before the barrier
+        // (they are operands of it), so that its first MFMAs issue right after.
+        const int pw_n = pw >= 3 ? pw - 3 : pw + 2;      // (pw + 2) % 5
+        const int px_n = pw_n == 4 ? 0 : pw_n + 1;
+        const int bx1_n = pw_n >= 2 ? pw_n - 2 : pw_n + 3;
+        const int bw2_n = pw_n >= 1 ? pw_n - 1 : 4;
+        const uint32_t wb_n = buf_addr(pw_n), xb_n = buf_addr(px_n);
+        const uint32_t lx_n = buf_addr(bx1_n), lw_n = buf_addr(bw2_n);
+        const uint32_t wa0_n = wb_n + wl[0], xa0_n = xb_n + xl[0];
+        asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(HLOADS), "s"(wb_n),
+                     "s"(xb_n), "s"(lx_n), "s"(lw_n), "v"(wa0_n), "v"(xa0_n) : "memory");
+        pw = pw_n;
+        wb = wb_n;
+        xb = xb_n;
+        lx = lx_n;
+        lw = lw_n;
+        wa0 = wa0_n;
+        xa0 = xa0_n;
     };
 
     // ---- epilogue: one head (128 columns) per wave ----------------------------
@@ -710,11 +731,11 @@ void fused_qkv_kernel(FusedArgs a) {
 
     // prologue: W and X halves of K-step 0 and the W half of K-step 1
 #pragma unroll
-    for (int i = 0; i < HLOADS; ++i) load_one(true, i, 0, 0);
+    for (int i = 0; i < HLOADS; ++i) load_one(true, i, 0, buf_addr(0));
 #pragma unroll
-    for (int i = 0; i < HLOADS; ++i) load_one(false, i, 0, 1);
+    for (int i = 0; i < HLOADS; ++i) load_one(false, i, 0, buf_addr(1));
 #pragma unroll
-    for (int i = 0; i < HLOADS; ++i) load_one(true, i, 1, 2);
+    for (int i = 0; i < HLOADS; ++i) load_one(true, i, 1, buf_addr(2));
     asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(HLOADS) : "memory");
     for (;;) {
         step(0, true);
