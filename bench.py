@@ -185,11 +185,12 @@ def pct(ms):
 
 
 def evict_caches(torch, evict):
-    """Read the 1 GiB buffer ``evict`` (more than the 256 MB MALL and the L2s):
-    afterwards the caches hold clean lines of it and none of the next kernel's
-    inputs.  (A write fill would leave dirty lines whose write-back then falls
-    inside the next timed region.)"""
-    return evict.view(torch.int32).sum(dtype=torch.int64)
+    """Read the 1 GiB buffer ``evict`` (more than the 256 MB MALL and the 8 x 4 MB
+    L2s; a float32 sum, which reads it in ~0.27 ms): afterwards the caches hold
+    clean lines of it and none of the next kernel's inputs.  (A write fill would
+    leave dirty lines whose write-back then falls inside the next timed
+    region.)"""
+    return evict.view(torch.float32).sum()
 
 
 WARMUP_S = 0.05                # device time of warm-up launches before a timed series
@@ -256,48 +257,60 @@ def back_to_back_us(torch, fn, stream, reps: int = 20) -> float:
     return e0.elapsed_time(e1) * 1e3 / reps
 
 
-def cold_us(torch, fn, stream, evict, reps: int = 10) -> float:
-    """Median time of ``fn`` (one or several launches, between one pair of
-    events) right after a read of the 1 GiB ``evict`` buffer, so that its
-    inputs come from HBM."""
-    fn()
-    torch.cuda.synchronize()
-    out = []
-    for _ in range(reps):
-        evict_caches(torch, evict)
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
+def cold_us(torch, fn, stream, evict, reps: int = 10, rounds: int = 5) -> float:
+    """Time of ``fn`` (one or several launches) when its inputs come from HBM:
+    ``reps`` x (read of the 1 GiB ``evict`` buffer, then ``fn``) back to back
+    between one pair of events, minus ``reps`` reads alone, per rep; median over
+    ``rounds`` alternating pairs of series.  Launches stay back to back, so
+    no pair of events falls around a short kernel (a pair around a near-empty
+    kernel measures ~6 us, against ~2 us for the same kernel back to back)."""
+    ev = lambda: evict_caches(torch, evict)
+
+    def both():
+        ev()
         fn()
-        e1.record(stream)
-        torch.cuda.synchronize()
-        out.append(e0.elapsed_time(e1) * 1e3)
-    return float(np.median(out))
+
+    alone, with_fn = [], []
+    for _ in range(rounds):
+        alone.append(back_to_back_us(torch, ev, stream, reps))
+        with_fn.append(back_to_back_us(torch, both, stream, reps))
+    return float(np.median(with_fn) - np.median(alone))
+
+
+COPY_SIZES = {"1GiB": 1 << 30,
+              # the read bytes of the 56-head U4 merge chunks of two and ten heads
+              "merge_chunk_2_heads": 4 * 9472 * 2 * 256,
+              "merge_chunk_10_heads": 4 * 9472 * 10 * 256}
 
 
 def copy_ceiling(torch, dev, stream, evict):
-    """The practical HBM ceiling: a plain 1 GiB device-to-device copy (torch's
-    copy kernel), back to back and from cold caches; bytes read + written."""
+    """The practical HBM ceiling: plain contiguous device-to-device copies, back
+    to back and from HBM (``cold_us``); bytes read + written.  At 1 GiB: torch's
+    copy kernel and the library's 16-byte streaming copy (the exchange_chunks
+    kernel with one peer); at the byte counts of the merge chunks: the library
+    copy, which shows what a launch of that size reaches from HBM at best."""
     import head_exchange_amd as hx
-    src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
-    src.fill_(1)
-    dst = torch.empty_like(src)
-    nbytes = 2.0 * src.numel()
-    out = {"bytes": nbytes}
-    # torch's copy kernel, and the library's own 16-byte streaming copy (the
-    # exchange_chunks kernel with one peer)
-    cases = {"torch_copy": lambda: dst.copy_(src),
-             "library_copy": lambda: hx.ulysses_exchange_chunks(src.view(1, -1), world=1, rank=0,
-                                                                 dst=[dst.view(1, -1)],
-                                                                 stream=stream)}
-    for name, fn in cases.items():
-        warm = back_to_back_us(torch, fn, stream, 10)
-        cold = cold_us(torch, fn, stream, evict, 5)
-        out[name] = {"warm_us": warm, "warm_gbps": nbytes / (warm * 1e-6) / 1e9,
-                     "warm_frac": nbytes / (warm * 1e-6) / 1e9 / PEAK_HBM_GBPS,
-                     "cold_us": cold, "cold_gbps": nbytes / (cold * 1e-6) / 1e9,
-                     "cold_frac": nbytes / (cold * 1e-6) / 1e9 / PEAK_HBM_GBPS}
-    del src, dst
-    torch.cuda.empty_cache()
+    out = {}
+    for label, size in COPY_SIZES.items():
+        src = torch.empty(size, dtype=torch.uint8, device=dev)
+        src.fill_(1)
+        dst = torch.empty_like(src)
+        nbytes = 2.0 * size
+        cases = {"library_copy": lambda: hx.ulysses_exchange_chunks(
+            src.view(1, -1), world=1, rank=0, dst=[dst.view(1, -1)], stream=stream)}
+        if label == "1GiB":
+            cases["torch_copy"] = lambda: dst.copy_(src)
+        res = {"bytes": nbytes}
+        for name, fn in cases.items():
+            warm = back_to_back_us(torch, fn, stream, 10)
+            cold = cold_us(torch, fn, stream, evict)
+            res[name] = {"warm_us": warm, "warm_gbps": nbytes / (warm * 1e-6) / 1e9,
+                         "warm_frac": nbytes / (warm * 1e-6) / 1e9 / PEAK_HBM_GBPS,
+                         "cold_us": cold, "cold_gbps": nbytes / (cold * 1e-6) / 1e9,
+                         "cold_frac": nbytes / (cold * 1e-6) / 1e9 / PEAK_HBM_GBPS}
+        out[label] = res
+        del src, dst
+        torch.cuda.empty_cache()
     return out
 
 
@@ -318,6 +331,7 @@ def sweep(hx, torch, W, dev, reps: int = 10):
     written by the band copy for pack and merge."""
     stream = torch.cuda.current_stream()
     evict = torch.empty(EVICT_BYTES, dtype=torch.uint8, device=dev)
+    evict.fill_(3)
     out = {}
     for name in SWEEP:
         wl = W.WORKLOADS[name]
@@ -742,11 +756,14 @@ def main():
             hx.ulysses_pack_qkv_head_chunk(q, k, v, world=U, schedule=wl.schedule, chunk=c,
                                            dst=pack_dst[c], row_offset=wl.rank * S, stream=stream)
 
+    def merge_chunk(c):
+        hx.ulysses_merge_output_head_chunk(merge_src, world=U, local_heads=hl,
+                                           schedule=wl.schedule, chunk=c, out=merge_out,
+                                           head_offset=sched[c][0], stream=stream)
+
     def merge_group():
-        for c, (off, _) in enumerate(sched):
-            hx.ulysses_merge_output_head_chunk(merge_src, world=U, local_heads=hl,
-                                               schedule=wl.schedule, chunk=c, out=merge_out,
-                                               head_offset=off, stream=stream)
+        for c in range(len(sched)):
+            merge_chunk(c)
 
     def step(ev=None):
         if ev is not None:
@@ -797,6 +814,11 @@ def main():
     evict.fill_(3)
     pack_cold_us = cold_us(torch, pack_group, stream, evict)
     merge_cold_us = cold_us(torch, merge_group, stream, evict)
+    merge_chunk_bytes = [2.0 * B * S * U * cnt * 128 * 2 for _, cnt in sched]
+    merge_chunk_cold = [cold_us(torch, lambda c=c: merge_chunk(c), stream, evict)
+                        for c in range(len(sched))]
+    merge_chunk_warm = [back_to_back_us(torch, lambda c=c: merge_chunk(c), stream)
+                        for c in range(len(sched))]
     ceiling = copy_ceiling(torch, dev, stream, evict)
     del evict
     torch.cuda.empty_cache()
@@ -837,8 +859,15 @@ def main():
                           "merge_us": merge_rep_ms * 1e3,
                           "merge_frac": merge_bytes / (merge_rep_ms * 1e-3) / 1e9 / PEAK_HBM_GBPS},
                       "cold": {
-                          "note": "each chunk group right after a read of a 1 GiB buffer "
-                                  "(inputs from HBM); median of 10",
+                          "note": "inputs from HBM: 10 x (read of a 1 GiB buffer, then the "
+                                  "group) back to back minus 10 reads alone, per group; "
+                                  "median of 5",
+                          "merge_chunks": [
+                              {"heads": cnt, "bytes": nb, "warm_us": wu,
+                               "warm_frac": nb / (wu * 1e-6) / 1e9 / PEAK_HBM_GBPS,
+                               "cold_us": cu, "cold_frac": nb / (cu * 1e-6) / 1e9 / PEAK_HBM_GBPS}
+                              for (_, cnt), nb, wu, cu in zip(sched, merge_chunk_bytes,
+                                                              merge_chunk_warm, merge_chunk_cold)],
                           "pack_us": pack_cold_us,
                           "pack_frac": pack_bytes / (pack_cold_us * 1e-6) / 1e9 / PEAK_HBM_GBPS,
                           "merge_us": merge_cold_us,
