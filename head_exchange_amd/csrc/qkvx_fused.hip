@@ -46,12 +46,14 @@
 //  * Persistent: one workgroup per CU, and the K-steps of a workgroup's
 //    consecutive output tiles form one continuous load stream, so the next
 //    tile's first K-steps are in flight while the current tile's epilogue
-//    runs.  The 8 XCDs (workgroup b runs on XCD b % 8) take consecutive ranges
-//    of a tile order that walks groups of tile rows column by column, so the
-//    tiles an XCD runs together share X and W panels in its L2.  Each XCD runs
-//    at its own clock under this load, so past two fixed rounds workgroups
-//    claim tiles one at a time from per-XCD counters (then from the other
-//    XCDs' ranges), and all XCDs finish together.
+//    runs.  The 8 XCDs (workgroup b runs on XCD b % 8) each own a run of tile
+//    rows and walk it column by column, all starting at column 0 (row bands
+//    when X is larger than the MALL): the tiles an XCD runs together share X
+//    and W panels in its L2, and the XCDs stream the W column panels in step,
+//    so that each comes from HBM about once and is then read from the MALL.
+//    Each XCD runs at its own clock under this load, so past two fixed rounds
+//    workgroups claim tiles one at a time from per-XCD counters (then from
+//    the other XCDs' queues), and all XCDs finish together.
 //  * Epilogue: Q/K norm and RoPE in registers, with the weights and cos/sin
 //    values loaded one step ahead (the first before the tile's last K-step);
 //    lanes of tokens 16 apart trade pieces so that each (nontemporal) store
@@ -102,19 +104,6 @@ __device__ __forceinline__ int lds_swz(int r) { return 2 * ((r >> 3) & 3) + ((r 
 // rows 32 h + 8 g .. + 7, and block blk + 4 holds the rows 64 further on.
 __device__ __forceinline__ int mfma_row(int blk, int i) {
     return 32 * (blk >> 1) + 8 * (i >> 2) + 4 * (blk & 1) + (i & 3);
-}
-
-// Tile coordinates of logical tile l: groups of group_m tile rows, walked
-// column by column.
-__device__ __forceinline__ void tile_coords(int l, int tiles_m, int tiles_n, int group_m,
-                                            int& tm, int& tn) {
-    const int in_group = group_m * tiles_n;
-    const int g = l / in_group;
-    const int first_m = g * group_m;
-    const int gsize = min(tiles_m - first_m, group_m);
-    const int r = l - g * in_group;
-    tm = first_m + r % gsize;
-    tn = r / gsize;
 }
 
 // Two floats rounded to bf16 (nearest even) and packed, lo in bits 0-15: one
@@ -197,39 +186,26 @@ void fused_qkv_kernel(FusedArgs a) {
     const int wm = wave >> 1;     // which 128 tokens of the tile
 
     // ---- tile schedule ---------------------------------------------------------
-    // The logical tile order is split into queues, one per XCD (workgroups b
-    // with b % 8 == x run on XCD x), or a single queue for a grid that is not
-    // a multiple of 8.  Queue x holds a contiguous share of the order; with
-    // readiness words the order is destination-major and is shared out one
-    // destination at a time (queue x: its share of destination 0's tiles,
-    // then of destination 1's, ...), so that destinations complete one after
-    // another while each XCD keeps runs of neighbouring tiles.  A queue's
-    // workgroups take its first two rounds (one tile each per round) in a
-    // fixed order; with tile-claim counters the rest is claimed one tile at a
-    // time (the workgroup's own queue first, then the others once it is used
-    // up), so that XCDs running at a higher clock take more tiles and all
-    // finish together.  Without counters the workgroups walk their queue a
-    // round at a time.
+    // The tile order (TileOrder: XCD-lockstep bands, destination-major with
+    // readiness words, or grouped) is split into queues, one per XCD
+    // (workgroups b with b % 8 == x run on XCD x), or a single queue for a grid
+    // that is not a multiple of 8.  A queue's workgroups take its first two
+    // rounds (one tile each per round) in a fixed order; with tile-claim
+    // counters the rest is claimed one tile at a time (the workgroup's own
+    // queue first, then the others once it is used up), so that XCDs running
+    // at a higher clock, or holding fewer tiles, take more and all finish
+    // together.  Without counters the workgroups walk their queue a round at a
+    // time.
     const int G = gridDim.x;
     const int bid = blockIdx.x;
-    const int total = a.tiles_m * a.tiles_n;
     const bool by_xcd = G % NXCD == 0;
     const int nq = by_xcd ? NXCD : 1;
     const bool claim = a.sched != nullptr;
-    // span: the tiles shared out among the queues at a time (one destination's
-    // tiles, world of them in all, or the whole order)
-    const int span = a.ready && a.dest_cols > 0 ? a.tiles_m * 3 * a.dest_cols : total;
-    const int nspan = total / span;
-    const int per = span / nq, rem = span % nq;
-    auto share_start = [&](int x) { return x * per + min(x, rem); };
-    auto share_len = [&](int x) { return per + (x < rem ? 1 : 0); };
-    auto qlen = [&](int x) { return nspan * share_len(x); };
+    const TileOrder order(a.tiles_m, a.tiles_n, a.group_m, nq, by_xcd ? a.bands : 0,
+                          a.ready ? a.dest_cols : 0, a.part_cols);
+    auto qlen = [&](int x) { return order.len(x); };
     // logical tile at position i < qlen(x) of queue x
-    auto qtile = [&](int x, int i) {
-        const int len = share_len(x);
-        const int sp = i / len;
-        return sp * span + share_start(x) + (i - sp * len);
-    };
+    auto qtile = [&](int x, int i) { return order.logical(x, i); };
     const int xcd = by_xcd ? bid % NXCD : 0;        // the workgroup's queue
     const int stride = by_xcd ? G / NXCD : G;       // workgroups per queue
     const int qfirst = by_xcd ? bid / NXCD : bid;   // its first position in the queue
@@ -252,23 +228,12 @@ void fused_qkv_kernel(FusedArgs a) {
     }
     const int first = qtile(xcd, qfirst);
     const int K = a.K;
-    // With readiness words the order is destination-major: the tiles holding
-    // destination d's heads (dest_cols columns in each of q, k, v) come before
-    // those of d + 1, so early destinations are complete early.
-    // n_own: the first output column the tile is responsible for (before the
-    // move back), which decides the heads it counts in the readiness words.
+    // Origin of logical tile l.  n_own: the first output column the tile is
+    // responsible for (before the move back), which decides the heads it
+    // counts in the readiness words.
     auto tile_origin = [&](int l, int& m0, int& n0, int& n_own) {
         int tm, tn;
-        if (a.ready && a.dest_cols > 0) {
-            const int per_dest = a.tiles_m * 3 * a.dest_cols;
-            const int d = l / per_dest;
-            int c;
-            tile_coords(l - d * per_dest, a.tiles_m, 3 * a.dest_cols, a.group_m, tm, c);
-            const int p = c / a.dest_cols;
-            tn = p * a.part_cols + d * a.dest_cols + (c - p * a.dest_cols);
-        } else {
-            tile_coords(l, a.tiles_m, a.tiles_n, a.group_m, tm, tn);
-        }
+        order.coords(l, tm, tn);
         m0 = tm * BM;
         n0 = tn * BN;
         n_own = n0;
@@ -887,6 +852,7 @@ hipError_t launch_fused(const FusedArgs& a_in, hipStream_t stream) {
     const int all_cus = device_cus();
     const int cus = a.ready && all_cus > 2 * NXCD ? all_cus - NXCD : all_cus;
     const int grid = tiles < cus ? tiles : cus;
+    a.bands = lockstep_bands(a.tiles_m, a.K, BM, grid, NXCD, a.ready != nullptr);
     auto kernel = a.M < BM ? (a.rope_interleaved ? fused_qkv_kernel<true, true>
                                                  : fused_qkv_kernel<true, false>)
                            : (a.rope_interleaved ? fused_qkv_kernel<false, true>

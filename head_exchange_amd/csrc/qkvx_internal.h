@@ -43,8 +43,117 @@ struct FastDiv {
 };
 
 // ---------------------------------------------------------------------------
-// fused projection kernel arguments
+// fused projection kernel: tile order and arguments
 // ---------------------------------------------------------------------------
+
+// The order in which a fused launch runs its tiles_m x tiles_n output tiles,
+// split into nq queues (one per XCD; one for a grid that is not a multiple of
+// the XCD count).  Position i < len(x) of queue x names logical tile
+// logical(x, i); coords() turns a logical tile into its tile row and column.
+// Three orders:
+//  * bands > 0 (XCD-lockstep): the tile rows are split into `bands` near-equal
+//    bands, run one after another.  In band b the rows are cut into nq
+//    near-equal runs; queue x owns run (x + b) % nq and walks it column by
+//    column.  Every queue starts a band at column 0, so the XCDs stream the
+//    W column panels in step (each comes from HBM about once per band and is
+//    then read from the MALL by the others) while the band's X rows stay in
+//    the MALL.  Logical tile l is row l / tiles_n, column l % tiles_n.
+//  * dest_cols > 0 (readiness words): destination-major; the tiles holding
+//    destination d's heads (dest_cols 256-column tiles in each of q, k, v)
+//    come before those of d + 1, and each destination's tiles (a span) are
+//    shared out among the queues in contiguous runs.
+//  * otherwise: groups of group_m tile rows walked column by column, shared
+//    out among the queues in contiguous runs.
+struct TileOrder {
+    int tiles_m, tiles_n, group_m, nq;
+    int bands;
+    int dest_cols, part_cols;
+    int span, nspan, per, rem;     // shared orders: tiles per span, spans, share sizes
+
+    __host__ __device__ TileOrder(int tm, int tn, int gm, int queues, int nbands, int dcols,
+                                  int pcols)
+        : tiles_m(tm), tiles_n(tn), group_m(gm), nq(queues), bands(nbands),
+          dest_cols(dcols), part_cols(pcols) {
+        const int total = tm * tn;
+        span = dcols > 0 ? tm * 3 * dcols : total;
+        nspan = total / span;
+        per = span / queues;
+        rem = span % queues;
+    }
+    // bands: first tile row of band b; the run of rows queue x owns in band b
+    __host__ __device__ int band_row(int b) const { return (tiles_m * b) / bands; }
+    __host__ __device__ int own_rows(int b, int x, int& r0) const {
+        const int b0 = band_row(b), rb = band_row(b + 1) - b0;
+        const int s = (x + b) % nq;
+        r0 = b0 + (rb * s) / nq;
+        return b0 + (rb * (s + 1)) / nq - r0;
+    }
+    __host__ __device__ int share_len(int x) const { return per + (x < rem ? 1 : 0); }
+    __host__ __device__ int len(int x) const {
+        if (bands > 0) {
+            int rows = 0, r0;
+            for (int b = 0; b < bands; ++b) rows += own_rows(b, x, r0);
+            return rows * tiles_n;
+        }
+        return nspan * share_len(x);
+    }
+    __host__ __device__ int logical(int x, int i) const {
+        if (bands > 0) {
+            int r0 = 0, r = 1;
+            for (int b = 0; b < bands; ++b) {
+                r = own_rows(b, x, r0);
+                if (i < r * tiles_n) break;
+                i -= r * tiles_n;
+            }
+            const int col = i / r;
+            return (r0 + (i - col * r)) * tiles_n + col;
+        }
+        const int ln = share_len(x);
+        const int sp = i / ln;
+        return sp * span + x * per + (x < rem ? x : rem) + (i - sp * ln);
+    }
+    // groups of group_m rows of a tiles_m x cols grid, walked column by column
+    __host__ __device__ void grouped(int l, int cols, int& tm, int& tn) const {
+        const int in_group = group_m * cols;
+        const int g = l / in_group;
+        const int first_m = g * group_m;
+        const int gsize = tiles_m - first_m < group_m ? tiles_m - first_m : group_m;
+        const int r = l - g * in_group;
+        tm = first_m + r % gsize;
+        tn = r / gsize;
+    }
+    __host__ __device__ void coords(int l, int& tm, int& tn) const {
+        if (bands > 0) {
+            tm = l / tiles_n;
+            tn = l - tm * tiles_n;
+        } else if (dest_cols > 0) {
+            const int d = l / span;
+            int c;
+            grouped(l - d * span, 3 * dest_cols, tm, c);
+            const int p = c / dest_cols;
+            tn = p * part_cols + d * dest_cols + (c - p * dest_cols);
+        } else {
+            grouped(l, tiles_n, tm, tn);
+        }
+    }
+};
+
+// Bytes of X tile rows a band of the XCD-lockstep order may hold: 7/8 of the
+// 256 MB MALL, the rest left to the W column panels in flight.
+constexpr int64_t kBandBytes = int64_t(224) << 20;
+
+// Bands of the XCD-lockstep order for a launch of `grid` workgroups on
+// tiles_m tile rows of K-deep X panels (BM rows each), or 0 where that order
+// does not apply: with readiness words (destination-major order), a grid that
+// is not a multiple of the XCD count, or fewer tile rows than XCDs.
+inline int lockstep_bands(int tiles_m, int K, int bm, int grid, int nxcd, bool ready) {
+    if (ready || grid % nxcd != 0 || tiles_m < nxcd) return 0;
+    const int64_t row_bytes = int64_t(bm) * K * 2;
+    int64_t max_rows = kBandBytes / row_bytes;
+    if (max_rows < nxcd) max_rows = nxcd;
+    return int((tiles_m + max_rows - 1) / max_rows);
+}
+
 struct FusedArgs {
     const uint16_t* x;        // [M, K] bf16
     const uint16_t* w;        // [N, K] bf16
@@ -61,7 +170,8 @@ struct FusedArgs {
     int32_t s_local;
     int32_t row0;             // rank * s_local: first sequence row and position
     int32_t tiles_m, tiles_n;
-    int32_t group_m;          // tile-row group of the tile order
+    int32_t group_m;          // tile-row group of the grouped tile orders
+    int32_t bands;            // > 0: row bands of the XCD-lockstep order (TileOrder)
     int32_t rope_interleaved; // 0: pairs (i, i + 64); 1: pairs (2i, 2i + 1)
     FastDiv div_s;            // by s_local: token -> (batch, sequence row); set at launch
     float eps;

@@ -1,0 +1,169 @@
+// Host check of the fused kernel's tile order (qkvx::TileOrder, the same code
+// the kernel runs) and of its tile-claim protocol.
+//  1. For every order (XCD-lockstep bands, destination-major, grouped), queue
+//     count and a range of grid shapes: the queue positions name every logical
+//     tile exactly once, and coords() maps the logical tiles one to one onto
+//     the tile grid.
+//  2. The claim protocol, simulated with seeded random interleavings of the
+//     workgroups: a workgroup takes positions qfirst and qfirst + stride of its
+//     queue, then claims positions from 2 * stride on through the queue's
+//     counter, moving on to the next queues once one is used up.  Every tile is
+//     run exactly once and every workgroup stops.
+//  3. lockstep_bands() on the benchmark shapes and its exclusions.
+// Prints "ok <count>" or the first failure.
+#include <cstdint>
+#include <cstdio>
+#include <random>
+#include <vector>
+
+#include "qkvx_internal.h"
+
+using qkvx::TileOrder;
+
+static int fails = 0;
+#define CHECK(c, ...)                         \
+    do {                                      \
+        if (!(c)) {                           \
+            if (fails++ < 5) {                \
+                printf("FAIL: " __VA_ARGS__); \
+                printf("\n");                 \
+            }                                 \
+        }                                     \
+    } while (0)
+
+static bool covers(const TileOrder& o) {
+    const int total = o.tiles_m * o.tiles_n;
+    std::vector<int> seen(total, 0), grid(total, 0);
+    for (int x = 0; x < o.nq; ++x)
+        for (int i = 0; i < o.len(x); ++i) {
+            const int l = o.logical(x, i);
+            if (l < 0 || l >= total) return false;
+            seen[l] += 1;
+        }
+    for (int l = 0; l < total; ++l) {
+        int tm, tn;
+        o.coords(l, tm, tn);
+        if (tm < 0 || tm >= o.tiles_m || tn < 0 || tn >= o.tiles_n) return false;
+        grid[tm * o.tiles_n + tn] += 1;
+    }
+    for (int l = 0; l < total; ++l)
+        if (seen[l] != 1 || grid[l] != 1) return false;
+    return true;
+}
+
+// The claim protocol of a launch of G workgroups (nq queues), one random
+// interleaving: returns true if every tile ran exactly once.
+static bool claims_cover(const TileOrder& o, int G, std::mt19937_64& rng) {
+    const int nq = o.nq, stride = G / nq;
+    const int total = o.tiles_m * o.tiles_n;
+    std::vector<unsigned> counter(nq, 0);
+    std::vector<int> ran(total, 0);
+    struct Wg { int xcd, cur, nxt, cvict, ctried; bool done; };
+    std::vector<Wg> wgs;
+    for (int b = 0; b < G; ++b) {
+        Wg w{nq == 1 ? 0 : b % nq, -1, -1, 0, 0, false};
+        const int qfirst = nq == 1 ? b : b / nq;
+        w.cvict = w.xcd;
+        if (qfirst >= o.len(w.xcd)) {
+            w.done = true;
+        } else {
+            w.cur = o.logical(w.xcd, qfirst);
+            w.nxt = qfirst + stride < o.len(w.xcd) ? o.logical(w.xcd, qfirst + stride) : -1;
+        }
+        wgs.push_back(w);
+    }
+    int live = 0;
+    for (auto& w : wgs) live += !w.done;
+    long guard = 0;
+    while (live > 0) {
+        if (++guard > 100L * total + 100000) return false;   // a workgroup that never stops
+        Wg& w = wgs[rng() % wgs.size()];
+        if (w.done) continue;
+        ran[w.cur] += 1;                                    // the current tile runs
+        if (w.nxt < 0) {
+            w.done = true;
+            --live;
+            continue;
+        }
+        int t = -1;
+        for (;;) {                                          // claim the tile after nxt
+            const int idx = 2 * stride + int(counter[w.cvict]++);
+            if (idx < o.len(w.cvict)) {
+                t = o.logical(w.cvict, idx);
+                break;
+            }
+            if (++w.ctried == nq) break;
+            w.cvict = w.cvict == nq - 1 ? 0 : w.cvict + 1;
+        }
+        w.cur = w.nxt;
+        w.nxt = t;
+    }
+    for (int l = 0; l < total; ++l)
+        if (ran[l] != 1) return false;
+    return true;
+}
+
+int main() {
+    std::mt19937_64 rng(20261203);
+    long checked = 0;
+    // 1 + 2: orders over grid shapes, queue counts and band counts
+    for (int tm = 1; tm <= 80; ++tm)
+        for (int tn : {1, 2, 3, 5, 12, 48, 72, 84}) {
+            for (int nq : {1, 8}) {
+                std::vector<int> band_counts = {0};
+                if (nq == 8 && tm >= 8)
+                    for (int b = 1; b <= 4 && tm / b >= 8; ++b) band_counts.push_back(b);
+                for (int bands : band_counts) {
+                    const TileOrder o(tm, tn, 8, nq, bands, 0, 0);
+                    CHECK(covers(o), "order tm %d tn %d nq %d bands %d", tm, tn, nq, bands);
+                    ++checked;
+                    const int total = tm * tn;
+                    for (int G : {8, 64, 248, 256}) {
+                        int g = total < G ? total : G;
+                        if (nq == 8 && g % 8 != 0) continue;
+                        if (nq == 1 && g % 8 == 0 && g > 1) g -= 1;
+                        if (g < 1) continue;
+                        for (int rep = 0; rep < 3; ++rep) {
+                            CHECK(claims_cover(o, g, rng), "claims tm %d tn %d nq %d bands %d G %d",
+                                  tm, tn, nq, bands, g);
+                            ++checked;
+                        }
+                    }
+                }
+            }
+        }
+    // destination-major orders: dest_cols tile columns per destination and part
+    for (int tm = 1; tm <= 40; ++tm)
+        for (int dc : {1, 2, 3, 7})
+            for (int world : {1, 2, 4, 8})
+                for (int nq : {1, 8}) {
+                    const int part_cols = dc * world;
+                    const TileOrder o(tm, 3 * part_cols, 8, nq, 0, dc, part_cols);
+                    CHECK(covers(o), "dest-major tm %d dc %d world %d nq %d", tm, dc, world, nq);
+                    const int total = tm * 3 * part_cols;
+                    int g = total < 248 ? total : 248;
+                    if (nq == 8) g -= g % 8;
+                    if (g >= 1) {
+                        CHECK(claims_cover(o, g, rng), "dest-major claims tm %d dc %d world %d", tm,
+                              dc, world);
+                        ++checked;
+                    }
+                    ++checked;
+                }
+    // 3: band counts of the benchmark shapes (256 x 256 tiles, 256 workgroups)
+    CHECK(qkvx::lockstep_bands(37, 7168, 256, 256, 8, false) == 1, "56-head U4 bands");
+    CHECK(qkvx::lockstep_bands(74, 7168, 256, 256, 8, false) == 2, "56-head U2 bands");
+    CHECK(qkvx::lockstep_bands(64, 6144, 256, 256, 8, false) == 1, "48-head U8 bands");
+    CHECK(qkvx::lockstep_bands(16, 4096, 256, 256, 8, false) == 1, "32-head bands");
+    CHECK(qkvx::lockstep_bands(37, 7168, 256, 248, 8, true) == 0, "readiness keeps its order");
+    CHECK(qkvx::lockstep_bands(7, 7168, 256, 256, 8, false) == 0, "fewer rows than XCDs");
+    CHECK(qkvx::lockstep_bands(37, 7168, 256, 250, 8, false) == 0, "grid not a multiple of 8");
+    CHECK(qkvx::lockstep_bands(400, 8192, 256, 256, 8, false) == 8, "bands of at most 50 rows");
+    checked += 8;
+    if (fails) {
+        printf("%d failures\n", fails);
+        return 1;
+    }
+    printf("ok %ld\n", checked);
+    return 0;
+}
