@@ -49,6 +49,10 @@ def parse():
                    help="target duration of the CPU oracle sample")
     p.add_argument("--skip-sweep", action="store_true",
                    help="do not time the other workloads and the cold-cache launches")
+    p.add_argument("--skip-power", action="store_true",
+                   help="do not sample power and clocks with amd-smi (for profiler runs: the "
+                        "tool is a script whose launcher replaces itself with its interpreter, "
+                        "which a process under the profiler's preload must not do)")
     return p.parse_args()
 
 
@@ -890,6 +894,9 @@ def main():
     for key, fn in (("power_under_fused_kernel",
                      lambda: sess.forward(x, w, wq, wk, cs, wl.rank, stream)),
                     ("power_under_reference_gemm", lambda: torch.mm(xm, wt))):
+        if args.skip_power:
+            result[key] = None
+            continue
         try:
             result[key] = power_sample(torch, fn)
         except Exception as exc:          # the samples are context; never fail the bench on them

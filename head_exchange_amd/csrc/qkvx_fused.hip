@@ -186,8 +186,8 @@ void fused_qkv_kernel(FusedArgs a) {
     const int wm = wave >> 1;     // which 128 tokens of the tile
 
     // ---- tile schedule ---------------------------------------------------------
-    // The tile order (TileOrder: XCD-lockstep bands, destination-major with
-    // readiness words, or grouped) is split into queues, one per XCD
+    // The tile order (TileOrder: destination by destination with readiness
+    // words; XCD-lockstep bands, or grouped rows) is split into queues, one per XCD
     // (workgroups b with b % 8 == x run on XCD x), or a single queue for a grid
     // that is not a multiple of 8.  A queue's workgroups take its first two
     // rounds (one tile each per round) in a fixed order; with tile-claim
@@ -852,7 +852,7 @@ hipError_t launch_fused(const FusedArgs& a_in, hipStream_t stream) {
     const int all_cus = device_cus();
     const int cus = a.ready && all_cus > 2 * NXCD ? all_cus - NXCD : all_cus;
     const int grid = tiles < cus ? tiles : cus;
-    a.bands = lockstep_bands(a.tiles_m, a.K, BM, grid, NXCD, a.ready != nullptr);
+    a.bands = lockstep_bands(a.tiles_m, a.K, BM, grid, NXCD);
     auto kernel = a.M < BM ? (a.rope_interleaved ? fused_qkv_kernel<true, true>
                                                  : fused_qkv_kernel<true, false>)
                            : (a.rope_interleaved ? fused_qkv_kernel<false, true>

@@ -50,33 +50,33 @@ struct FastDiv {
 // split into nq queues (one per XCD; one for a grid that is not a multiple of
 // the XCD count).  Position i < len(x) of queue x names logical tile
 // logical(x, i); coords() turns a logical tile into its tile row and column.
-// Three orders:
+// The tiles come in spans of tiles_m x cols tiles, run one after another: with
+// readiness words (dest_cols > 0) span d holds the tiles of destination d's
+// heads (dest_cols 256-column tiles in each of q, k and v, cols = 3 dest_cols),
+// so that early destinations complete early; otherwise the one span is the
+// whole grid.  Within a span:
 //  * bands > 0 (XCD-lockstep): the tile rows are split into `bands` near-equal
 //    bands, run one after another.  In band b the rows are cut into nq
 //    near-equal runs; queue x owns run (x + b) % nq and walks it column by
-//    column.  Every queue starts a band at column 0, so the XCDs stream the
-//    W column panels in step (each comes from HBM about once per band and is
-//    then read from the MALL by the others) while the band's X rows stay in
-//    the MALL.  Logical tile l is row l / tiles_n, column l % tiles_n.
-//  * dest_cols > 0 (readiness words): destination-major; the tiles holding
-//    destination d's heads (dest_cols 256-column tiles in each of q, k, v)
-//    come before those of d + 1, and each destination's tiles (a span) are
-//    shared out among the queues in contiguous runs.
-//  * otherwise: groups of group_m tile rows walked column by column, shared
+//    column.  Every queue starts a band at the span's first column, so the
+//    XCDs stream the W column panels in step (each comes from HBM about once
+//    per band and is then read from the MALL by the others) while the band's
+//    X rows stay in the MALL.
+//  * bands == 0: groups of group_m tile rows walked column by column, shared
 //    out among the queues in contiguous runs.
 struct TileOrder {
     int tiles_m, tiles_n, group_m, nq;
     int bands;
     int dest_cols, part_cols;
-    int span, nspan, per, rem;     // shared orders: tiles per span, spans, share sizes
+    int cols, span, nspan, per, rem;
 
     __host__ __device__ TileOrder(int tm, int tn, int gm, int queues, int nbands, int dcols,
                                   int pcols)
         : tiles_m(tm), tiles_n(tn), group_m(gm), nq(queues), bands(nbands),
           dest_cols(dcols), part_cols(pcols) {
-        const int total = tm * tn;
-        span = dcols > 0 ? tm * 3 * dcols : total;
-        nspan = total / span;
+        cols = dcols > 0 ? 3 * dcols : tn;
+        span = tm * cols;
+        nspan = (tm * tn) / span;
         per = span / queues;
         rem = span % queues;
     }
@@ -88,52 +88,54 @@ struct TileOrder {
         r0 = b0 + (rb * s) / nq;
         return b0 + (rb * (s + 1)) / nq - r0;
     }
-    __host__ __device__ int share_len(int x) const { return per + (x < rem ? 1 : 0); }
-    __host__ __device__ int len(int x) const {
+    // positions of queue x in one span
+    __host__ __device__ int span_len(int x) const {
         if (bands > 0) {
             int rows = 0, r0;
             for (int b = 0; b < bands; ++b) rows += own_rows(b, x, r0);
-            return rows * tiles_n;
+            return rows * cols;
         }
-        return nspan * share_len(x);
+        return per + (x < rem ? 1 : 0);
     }
+    __host__ __device__ int len(int x) const { return nspan * span_len(x); }
     __host__ __device__ int logical(int x, int i) const {
+        const int ln = span_len(x);
+        const int sp = i / ln;
+        i -= sp * ln;
         if (bands > 0) {
             int r0 = 0, r = 1;
             for (int b = 0; b < bands; ++b) {
                 r = own_rows(b, x, r0);
-                if (i < r * tiles_n) break;
-                i -= r * tiles_n;
+                if (i < r * cols) break;
+                i -= r * cols;
             }
             const int col = i / r;
-            return (r0 + (i - col * r)) * tiles_n + col;
+            return sp * span + (r0 + (i - col * r)) * cols + col;
         }
-        const int ln = share_len(x);
-        const int sp = i / ln;
-        return sp * span + x * per + (x < rem ? x : rem) + (i - sp * ln);
-    }
-    // groups of group_m rows of a tiles_m x cols grid, walked column by column
-    __host__ __device__ void grouped(int l, int cols, int& tm, int& tn) const {
-        const int in_group = group_m * cols;
-        const int g = l / in_group;
-        const int first_m = g * group_m;
-        const int gsize = tiles_m - first_m < group_m ? tiles_m - first_m : group_m;
-        const int r = l - g * in_group;
-        tm = first_m + r % gsize;
-        tn = r / gsize;
+        return sp * span + x * per + (x < rem ? x : rem) + i;
     }
     __host__ __device__ void coords(int l, int& tm, int& tn) const {
+        const int sp = l / span;
+        const int rr = l - sp * span;
+        int c;
         if (bands > 0) {
-            tm = l / tiles_n;
-            tn = l - tm * tiles_n;
-        } else if (dest_cols > 0) {
-            const int d = l / span;
-            int c;
-            grouped(l - d * span, 3 * dest_cols, tm, c);
-            const int p = c / dest_cols;
-            tn = p * part_cols + d * dest_cols + (c - p * dest_cols);
+            tm = rr / cols;
+            c = rr - tm * cols;
         } else {
-            grouped(l, tiles_n, tm, tn);
+            // groups of group_m rows, walked column by column
+            const int in_group = group_m * cols;
+            const int g = rr / in_group;
+            const int first_m = g * group_m;
+            const int gsize = tiles_m - first_m < group_m ? tiles_m - first_m : group_m;
+            const int r = rr - g * in_group;
+            tm = first_m + r % gsize;
+            c = r / gsize;
+        }
+        if (dest_cols > 0) {
+            const int p = c / dest_cols;
+            tn = p * part_cols + sp * dest_cols + (c - p * dest_cols);
+        } else {
+            tn = c;
         }
     }
 };
@@ -143,11 +145,11 @@ struct TileOrder {
 constexpr int64_t kBandBytes = int64_t(224) << 20;
 
 // Bands of the XCD-lockstep order for a launch of `grid` workgroups on
-// tiles_m tile rows of K-deep X panels (BM rows each), or 0 where that order
-// does not apply: with readiness words (destination-major order), a grid that
-// is not a multiple of the XCD count, or fewer tile rows than XCDs.
-inline int lockstep_bands(int tiles_m, int K, int bm, int grid, int nxcd, bool ready) {
-    if (ready || grid % nxcd != 0 || tiles_m < nxcd) return 0;
+// tiles_m tile rows of K-deep X panels (bm rows each), or 0 where that order
+// does not apply: a grid that is not a multiple of the XCD count, or fewer
+// tile rows than XCDs.
+inline int lockstep_bands(int tiles_m, int K, int bm, int grid, int nxcd) {
+    if (grid % nxcd != 0 || tiles_m < nxcd) return 0;
     const int64_t row_bytes = int64_t(bm) * K * 2;
     int64_t max_rows = kBandBytes / row_bytes;
     if (max_rows < nxcd) max_rows = nxcd;

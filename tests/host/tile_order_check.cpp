@@ -1,9 +1,9 @@
 // Host check of the fused kernel's tile order (qkvx::TileOrder, the same code
 // the kernel runs) and of its tile-claim protocol.
-//  1. For every order (XCD-lockstep bands, destination-major, grouped), queue
-//     count and a range of grid shapes: the queue positions name every logical
-//     tile exactly once, and coords() maps the logical tiles one to one onto
-//     the tile grid.
+//  1. For every order (XCD-lockstep bands or grouped rows, over the whole grid
+//     or destination by destination), queue count and a range of grid shapes:
+//     the queue positions name every logical tile exactly once, and coords()
+//     maps the logical tiles one to one onto the tile grid.
 //  2. The claim protocol, simulated with seeded random interleavings of the
 //     workgroups: a workgroup takes positions qfirst and qfirst + stride of its
 //     queue, then claims positions from 2 * stride on through the queue's
@@ -132,33 +132,38 @@ int main() {
                 }
             }
         }
-    // destination-major orders: dest_cols tile columns per destination and part
+    // destination by destination (readiness words): dest_cols tile columns per
+    // destination and part, grouped or in lockstep bands
     for (int tm = 1; tm <= 40; ++tm)
         for (int dc : {1, 2, 3, 7})
             for (int world : {1, 2, 4, 8})
-                for (int nq : {1, 8}) {
-                    const int part_cols = dc * world;
-                    const TileOrder o(tm, 3 * part_cols, 8, nq, 0, dc, part_cols);
-                    CHECK(covers(o), "dest-major tm %d dc %d world %d nq %d", tm, dc, world, nq);
-                    const int total = tm * 3 * part_cols;
-                    int g = total < 248 ? total : 248;
-                    if (nq == 8) g -= g % 8;
-                    if (g >= 1) {
-                        CHECK(claims_cover(o, g, rng), "dest-major claims tm %d dc %d world %d", tm,
-                              dc, world);
+                for (int nq : {1, 8})
+                    for (int bands = 0; bands <= 2; ++bands) {
+                        if (bands > 0 && (nq != 8 || tm / bands < 8)) continue;
+                        const int part_cols = dc * world;
+                        const TileOrder o(tm, 3 * part_cols, 8, nq, bands, dc, part_cols);
+                        CHECK(covers(o), "dest-major tm %d dc %d world %d nq %d bands %d", tm, dc,
+                              world, nq, bands);
+                        const int total = tm * 3 * part_cols;
+                        int g = total < 248 ? total : 248;
+                        if (nq == 8) g -= g % 8;
+                        if (g >= 1) {
+                            CHECK(claims_cover(o, g, rng),
+                                  "dest-major claims tm %d dc %d world %d bands %d", tm, dc, world,
+                                  bands);
+                            ++checked;
+                        }
                         ++checked;
                     }
-                    ++checked;
-                }
     // 3: band counts of the benchmark shapes (256 x 256 tiles, 256 workgroups)
-    CHECK(qkvx::lockstep_bands(37, 7168, 256, 256, 8, false) == 1, "56-head U4 bands");
-    CHECK(qkvx::lockstep_bands(74, 7168, 256, 256, 8, false) == 2, "56-head U2 bands");
-    CHECK(qkvx::lockstep_bands(64, 6144, 256, 256, 8, false) == 1, "48-head U8 bands");
-    CHECK(qkvx::lockstep_bands(16, 4096, 256, 256, 8, false) == 1, "32-head bands");
-    CHECK(qkvx::lockstep_bands(37, 7168, 256, 248, 8, true) == 0, "readiness keeps its order");
-    CHECK(qkvx::lockstep_bands(7, 7168, 256, 256, 8, false) == 0, "fewer rows than XCDs");
-    CHECK(qkvx::lockstep_bands(37, 7168, 256, 250, 8, false) == 0, "grid not a multiple of 8");
-    CHECK(qkvx::lockstep_bands(400, 8192, 256, 256, 8, false) == 8, "bands of at most 50 rows");
+    CHECK(qkvx::lockstep_bands(37, 7168, 256, 256, 8) == 1, "56-head U4 bands");
+    CHECK(qkvx::lockstep_bands(74, 7168, 256, 256, 8) == 2, "56-head U2 bands");
+    CHECK(qkvx::lockstep_bands(64, 6144, 256, 256, 8) == 1, "48-head U8 bands");
+    CHECK(qkvx::lockstep_bands(16, 4096, 256, 256, 8) == 1, "32-head bands");
+    CHECK(qkvx::lockstep_bands(37, 7168, 256, 248, 8) == 1, "readiness grid of 248");
+    CHECK(qkvx::lockstep_bands(7, 7168, 256, 256, 8) == 0, "fewer rows than XCDs");
+    CHECK(qkvx::lockstep_bands(37, 7168, 256, 250, 8) == 0, "grid not a multiple of 8");
+    CHECK(qkvx::lockstep_bands(400, 8192, 256, 256, 8) == 8, "bands of at most 50 rows");
     checked += 8;
     if (fails) {
         printf("%d failures\n", fails);
