@@ -526,14 +526,15 @@ int qkvx_describe(const qkvx_session* s, char* buf, size_t len) {
         "\"region_elems\": %lld, \"slot_bytes\": %zu, \"owns_slots\": %s, \"calls\": %lld, "
         "\"next_slot\": %d, \"rope\": \"%s\", \"publish\": %s, \"eps\": 1e-6, "
         "\"tile\": {\"block_m\": %d, \"block_n\": %d, \"block_k\": %d, \"threads\": %d, "
-        "\"group_m\": %d, \"mfma\": \"v_mfma_f32_16x16x32_bf16\", \"xcd_remap\": 8}}",
+        "\"group_m\": %d, \"mfma\": \"v_mfma_f32_16x16x32_bf16\", \"xcd_remap\": 8, "
+        "\"order\": \"xcd_lockstep\", \"band_bytes\": %lld}}",
         s->hidden, s->heads, QKVX_HEAD_DIM, s->world, s->heads / s->world,
         s->layout == QKVX_LAYOUT_BSHD ? "bshd" : "fused", (long long)s->max_tokens,
         s->num_slots, (long long)s->region_elems, s->slot_bytes, s->owns_slots ? "true" : "false",
         (long long)s->calls, int(s->calls % s->num_slots),
         s->rope == QKVX_ROPE_INTERLEAVED ? "interleaved" : "rotate_half",
         s->publish ? "true" : "false", p.block_m, p.block_n, p.block_k,
-        p.threads, p.group_m);
+        p.threads, p.group_m, (long long)kBandBytes);
     if (buf && len) {
         size_t c = size_t(n) < len ? size_t(n) : len - 1;
         memcpy(buf, tmp, c);

@@ -98,6 +98,7 @@ def test_create_and_describe_without_device(lib):
     d = json.loads(buf.value.decode())
     assert d["local_heads"] == 2 and d["owns_slots"] is False and d["next_slot"] == 0
     assert d["rope"] == "rotate_half"
+    assert d["tile"]["order"] == "xcd_lockstep" and d["tile"]["band_bytes"] == 224 << 20
     assert lib.qkvx_destroy(h) == 0
     st, h = create(lib, rope=1)
     n = lib.qkvx_describe(h, None, 0)
