@@ -177,6 +177,36 @@ def test_random_small_shapes(gpu_lib, seed):
                f"H{wl.heads} U{wl.world} r{wl.rank} {wl.layout} {rope}", rope=rope)
 
 
+# Launches of at least 256 tiles on 8 to 63 tile rows run the XCD-lockstep
+# tile order: each XCD owns a run of tile rows (here ragged runs of one to
+# three rows and a ragged last tile row), and workgroups claim the rest across
+# the queues.  With readiness words the same order runs destination by
+# destination (the second shape: five destinations of two tile columns per
+# part; the first has an odd local head count and keeps the plain order).
+MID = [
+    W.custom(60, batch=1, s_local=4531, heads=10, world=2, rank=1, layout="bshd",
+             schedule=(5,), rope_base=1e4),           # 18 x 15 tiles
+    W.custom(61, batch=2, s_local=1111, heads=20, world=5, rank=4, layout="fused",
+             schedule=(4,), rope_base=1e6),           # 9 x 30 tiles
+]
+
+
+@pytest.mark.parametrize("publish", [False, True])
+@pytest.mark.parametrize("wl", MID, ids=lambda w: w.name)
+def test_lockstep_order_mid_shapes(gpu_lib, wl, publish):
+    inp = Inputs(wl)
+    sess = make_session(gpu_lib, wl)
+    if publish:
+        sess.set_publish(True)
+    sess.poison_receive_slots()
+    views = run(sess, inp)
+    torch.cuda.synchronize()
+    check_full(views, inp, wl.rank, f"{wl.name}:publish={publish}")
+    if publish:
+        words, timeouts = sess.ready_state()
+        assert words == sess.ready_expected() and timeouts == 0
+
+
 @pytest.mark.parametrize("wl", SMALL[:3], ids=lambda w: w.name)
 def test_small_full_slots_interleaved_rope(gpu_lib, wl):
     """The pages' pairing (2i, 2i+1) selected at session creation."""
