@@ -15,7 +15,9 @@ algorithmic projection FLOPs (2*M*N*K) over the step time; per-kernel times
 come from HIP events recorded on the launch stream inside the timed region.
 
 Prints one JSON line.  Only --gpus 1 is supported (one GPU's share of the
-exchange; the peers are simulated in local HBM).
+exchange; the peers are simulated in local HBM).  --workload runs the same
+step on another of the named workloads (for counter profiles of those shapes);
+the reported metric is quoted on the 56-head Ulysses-4 shard.
 """
 from __future__ import annotations
 
@@ -31,16 +33,28 @@ import numpy as np
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
-WORKLOAD = "h56_u4"
+WORKLOAD = "h56_u4"               # the shard the metric is quoted on
 PEAK_BF16_TFLOPS = 2500.0       # MI355X dense bf16 MFMA
 PEAK_HBM_GBPS = 8000.0          # MI355X HBM3E
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fused_qkvx_h56_u4_traffic.txt")
+
+
+def traffic_file(workload: str) -> str:
+    return os.path.join(ROOT, "profiles", f"fused_qkvx_{workload}_traffic.txt")
+
+
+def mfma_file(workload: str) -> str:
+    return os.path.join(ROOT, "profiles", f"fused_qkvx_{workload}_mfma.txt")
+
+
 FUSED_SOURCE = os.path.join(ROOT, "head_exchange_amd", "csrc", "qkvx_fused.hip")
 
 
 def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--workload", default=WORKLOAD,
+                   choices=["h32_u4_fused", "h56_u4", "h56_u2_fused", "h48_u8_stress"],
+                   help="workload of the step (default: the 56-head Ulysses-4 shard)")
     p.add_argument("--steps", type=int, default=20)
     p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--skip-cpu-baseline", action="store_true",
@@ -66,13 +80,14 @@ def profile_label(path: str) -> str:
     return f"{os.path.relpath(path, ROOT)} @ kernel source {source_hash(FUSED_SOURCE)}"
 
 
-def read_traffic():
+def read_traffic(workload: str):
     """HBM bytes per launch of the fused kernel from the committed counter
     summary, or None when it is missing or the kernel changed since."""
-    if not os.path.exists(TRAFFIC_FILE):
+    path = traffic_file(workload)
+    if not os.path.exists(path):
         return None
     kv = {}
-    for line in open(TRAFFIC_FILE):
+    for line in open(path):
         if ":" in line and not line.startswith("#"):
             k, v = line.split(":", 1)
             kv[k.strip()] = v.strip()
@@ -156,17 +171,17 @@ def cpu_baseline(wl, x, w, wq, wk, cs, qkv_src, band, target_s: float):
             "seconds": round(dt, 2), "tokens": T}
 
 
-MFMA_FILE = os.path.join(ROOT, "profiles", "fused_qkvx_h56_u4_mfma.txt")
 SWEEP = ["h32_u4_fused", "h56_u4", "h56_u2_fused", "h48_u8_stress"]
 EVICT_BYTES = 1 << 30           # > the 256 MB MALL and the 8 x 4 MB L2s
 
 
-def read_mfma_counters():
+def read_mfma_counters(workload: str):
     """MFMA busy fraction and shader clock of the fused kernel from the committed
     counter summary, or None when it is missing or the kernel changed since."""
-    if not os.path.exists(MFMA_FILE):
+    path = mfma_file(workload)
+    if not os.path.exists(path):
         return None
-    text = open(MFMA_FILE).read()
+    text = open(path).read()
     if source_hash(FUSED_SOURCE) not in text:
         return None
     kv = {}
@@ -281,13 +296,16 @@ def cold_us(torch, fn, stream, evict, reps: int = 10, rounds: int = 5) -> float:
     return float(np.median(with_fn) - np.median(alone))
 
 
-COPY_SIZES = {"1GiB": 1 << 30,
-              # the read bytes of the 56-head U4 merge chunks of two and ten heads
-              "merge_chunk_2_heads": 4 * 9472 * 2 * 256,
-              "merge_chunk_10_heads": 4 * 9472 * 10 * 256}
+def copy_sizes(wl) -> dict:
+    """1 GiB, and the read bytes of each distinct merge chunk of the workload."""
+    import workloads as W
+    sizes = {"1GiB": 1 << 30}
+    for _, cnt in W.schedule_pairs(wl.schedule):
+        sizes[f"merge_chunk_{cnt}_heads"] = wl.batch * wl.s_local * wl.world * cnt * 256
+    return sizes
 
 
-def copy_ceiling(torch, dev, stream, evict):
+def copy_ceiling(torch, dev, stream, evict, wl):
     """The practical HBM ceiling: plain contiguous device-to-device copies, back
     to back and from HBM (``cold_us``); bytes read + written.  At 1 GiB: torch's
     copy kernel and the library's 16-byte streaming copy (the exchange_chunks
@@ -295,7 +313,7 @@ def copy_ceiling(torch, dev, stream, evict):
     copy, which shows what a launch of that size reaches from HBM at best."""
     import head_exchange_amd as hx
     out = {}
-    for label, size in COPY_SIZES.items():
+    for label, size in copy_sizes(wl).items():
         src = torch.empty(size, dtype=torch.uint8, device=dev)
         src.fill_(1)
         dst = torch.empty_like(src)
@@ -728,7 +746,7 @@ def main():
     hx.load()
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    wl = W.WORKLOADS[WORKLOAD]
+    wl = W.WORKLOADS[args.workload]
     M, N, K = wl.gemm_shape
     S, U, hl, B = wl.s_local, wl.world, wl.local_heads, wl.batch
     sched = W.schedule_pairs(wl.schedule)
@@ -802,7 +820,7 @@ def main():
     pack_bytes = sum(2.0 * B * S * U * cnt * 384 * 2 for _, cnt in sched)
     merge_bytes = sum(2.0 * B * S * U * cnt * 128 * 2 for _, cnt in sched)
     achieved = flops / (fused_ms * 1e-3) / 1e12
-    traffic = read_traffic()
+    traffic = read_traffic(args.workload)
 
     # The same pack and merge groups REPS times back to back between one pair
     # of events: the per-group time without the cost of the events themselves,
@@ -823,7 +841,7 @@ def main():
                         for c in range(len(sched))]
     merge_chunk_warm = [back_to_back_us(torch, lambda c=c: merge_chunk(c), stream)
                         for c in range(len(sched))]
-    ceiling = copy_ceiling(torch, dev, stream, evict)
+    ceiling = copy_ceiling(torch, dev, stream, evict, wl)
     del evict
     torch.cuda.empty_cache()
 
@@ -840,11 +858,11 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": WORKLOAD, "batch": B, "s_local": S, "s_global": wl.s_global,
+        "config": {"workload": args.workload, "batch": B, "s_local": S, "s_global": wl.s_global,
                    "heads": wl.heads, "head_dim": 128, "hidden": wl.hidden, "world": U,
                    "rank": wl.rank, "layout": wl.layout, "schedule": list(wl.schedule),
                    "gemm_mnk": [M, N, K], "rope": "rotate_half", "rope_base": wl.rope_base,
-                   "parallelism": "ulysses shard of 4 (peers simulated in local HBM)"},
+                   "parallelism": f"ulysses shard of {U} (peers simulated in local HBM)"},
         "roofline": {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS,
                      "traffic": traffic, "kernel": "fused_qkv_kernel",
@@ -884,11 +902,11 @@ def main():
         "kernels_pct": {n: pct(v) for n, v in per.items()},
     }
     if traffic is not None:
-        result["roofline"]["traffic_from"] = profile_label(TRAFFIC_FILE)
-    counters = read_mfma_counters()
+        result["roofline"]["traffic_from"] = profile_label(traffic_file(args.workload))
+    counters = read_mfma_counters(args.workload)
     if counters:
         result["roofline"].update(counters)
-        result["roofline"]["counters_from"] = profile_label(MFMA_FILE)
+        result["roofline"]["counters_from"] = profile_label(mfma_file(args.workload))
     result["reference_gemm"] = reference_gemm(torch, x, w, stream)
     xm, wt = x.view(-1, x.shape[-1]), w.t()
     for key, fn in (("power_under_fused_kernel",
