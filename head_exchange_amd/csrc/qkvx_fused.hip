@@ -53,7 +53,7 @@
 //    so that each comes from HBM about once and is then read from the MALL.
 //    Each XCD runs at its own clock under this load, so past two fixed rounds
 //    workgroups claim tiles one at a time from per-XCD counters (then from
-//    the other XCDs' queues), and all XCDs finish together.
+//    the other XCDs' queues, the fullest first), and all XCDs finish together.
 //  * Epilogue: Q/K norm and RoPE in registers, with the weights and cos/sin
 //    values loaded one step ahead (the first before the tile's last K-step);
 //    lanes of tokens 16 apart trade pieces so that each (nontemporal) store
@@ -192,9 +192,9 @@ void fused_qkv_kernel(FusedArgs a) {
     // that is not a multiple of 8.  A queue's workgroups take its first two
     // rounds (one tile each per round) in a fixed order; with tile-claim
     // counters the rest is claimed one tile at a time (the workgroup's own
-    // queue first, then the others once it is used up), so that XCDs running
-    // at a higher clock, or holding fewer tiles, take more and all finish
-    // together.  Without counters the workgroups walk their queue a round at a
+    // queue first; once it is used up, the queue with the most tiles left), so
+    // that XCDs running at a higher clock, or holding fewer tiles, take more
+    // and all finish together.  Without counters the workgroups walk their queue a round at a
     // time.
     const int G = gridDim.x;
     const int bid = blockIdx.x;
@@ -690,9 +690,8 @@ void fused_qkv_kernel(FusedArgs a) {
     __builtin_amdgcn_sched_barrier(0);
   };
 
-    // claim state (thread 0 only): the queue counter being drawn from, and how
-    // many counters were found used up
-    int cvict = xcd, ctried = 0;
+    // claim state (thread 0 only): the queue counter being drawn from
+    int cvict = xcd;
 
     // prologue: W and X halves of K-step 0 and the W half of K-step 1
 #pragma unroll
@@ -758,8 +757,29 @@ void fused_qkv_kernel(FusedArgs a) {
                         t = qtile(cvict, idx);
                         break;
                     }
-                    if (++ctried == nq) break;
-                    cvict = cvict == nq - 1 ? 0 : cvict + 1;
+                    // This queue is used up: read every queue's counter at once
+                    // (independent loads, one round trip) and claim from the one
+                    // with the most tiles left; none left ends the workgroup's
+                    // claims.  Counters only grow, so a count read here never
+                    // overstates what is left, and each claim moves one on.
+                    int best = -1, most = 0;
+                    unsigned int seen[NXCD];
+#pragma unroll
+                    for (int q = 0; q < NXCD; ++q)
+                        if (q < nq)
+                            seen[q] = __hip_atomic_load(a.sched + q, __ATOMIC_RELAXED,
+                                                        __HIP_MEMORY_SCOPE_AGENT);
+#pragma unroll
+                    for (int q = 0; q < NXCD; ++q)
+                        if (q < nq) {
+                            const int left = qlen(q) - (2 * stride + int(seen[q]));
+                            if (left > most) {
+                                most = left;
+                                best = q;
+                            }
+                        }
+                    if (best < 0) break;
+                    cvict = best;
                     reply = __hip_atomic_fetch_add(a.sched + cvict, 1u, __ATOMIC_RELAXED,
                                                    __HIP_MEMORY_SCOPE_AGENT);
                 }

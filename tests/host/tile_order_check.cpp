@@ -7,8 +7,9 @@
 //  2. The claim protocol, simulated with seeded random interleavings of the
 //     workgroups: a workgroup takes positions qfirst and qfirst + stride of its
 //     queue, then claims positions from 2 * stride on through the queue's
-//     counter, moving on to the next queues once one is used up.  Every tile is
-//     run exactly once and every workgroup stops.
+//     counter; once that queue is used up it reads every counter and claims
+//     from the queue with the most positions left, until none is left.  Every
+//     tile is run exactly once and every workgroup stops.
 //  3. lockstep_bands() on the benchmark shapes and its exclusions.
 // Prints "ok <count>" or the first failure.
 #include <cstdint>
@@ -58,10 +59,10 @@ static bool claims_cover(const TileOrder& o, int G, std::mt19937_64& rng) {
     const int total = o.tiles_m * o.tiles_n;
     std::vector<unsigned> counter(nq, 0);
     std::vector<int> ran(total, 0);
-    struct Wg { int xcd, cur, nxt, cvict, ctried; bool done; };
+    struct Wg { int xcd, cur, nxt, cvict; bool done; };
     std::vector<Wg> wgs;
     for (int b = 0; b < G; ++b) {
-        Wg w{nq == 1 ? 0 : b % nq, -1, -1, 0, 0, false};
+        Wg w{nq == 1 ? 0 : b % nq, -1, -1, 0, false};
         const int qfirst = nq == 1 ? b : b / nq;
         w.cvict = w.xcd;
         if (qfirst >= o.len(w.xcd)) {
@@ -86,14 +87,24 @@ static bool claims_cover(const TileOrder& o, int G, std::mt19937_64& rng) {
             continue;
         }
         int t = -1;
-        for (;;) {                                          // claim the tile after nxt
-            const int idx = 2 * stride + int(counter[w.cvict]++);
+        int reply = int(counter[w.cvict]++);               // claim the tile after nxt
+        for (;;) {
+            const int idx = 2 * stride + reply;
             if (idx < o.len(w.cvict)) {
                 t = o.logical(w.cvict, idx);
                 break;
             }
-            if (++w.ctried == nq) break;
-            w.cvict = w.cvict == nq - 1 ? 0 : w.cvict + 1;
+            int best = -1, most = 0;                        // the fullest queue left
+            for (int q = 0; q < nq; ++q) {
+                const int left = o.len(q) - (2 * stride + int(counter[q]));
+                if (left > most) {
+                    most = left;
+                    best = q;
+                }
+            }
+            if (best < 0) break;
+            w.cvict = best;
+            reply = int(counter[w.cvict]++);
         }
         w.cur = w.nxt;
         w.nxt = t;
