@@ -10,11 +10,13 @@
 //
 // Design (gfx950):
 //  * The GEMM is computed transposed, C^T[n, m] = W[n, :] . X[m, :], with
-//    v_mfma_f32_16x16x32_bf16.  Under the chip's power limit this form does
-//    13 % more work than v_mfma_f32_32x32x16_bf16 (it moves half the
-//    accumulator bytes per multiply-add).  In the 16x16 accumulator layout a
-//    lane owns one column (here: one token) and four rows (here: head dims) of
-//    a block, and the four lanes l + 16 g share the token.  A wave's 128-row
+//    v_mfma_f32_16x16x32_bf16.  Under the chip's power limit the kernel runs
+//    at a 13 % higher clock with this form than with v_mfma_f32_32x32x16_bf16
+//    (it moves half the accumulator bytes per multiply-add), which more than
+//    pays for the load issue the longer form would hide.  In the 16x16
+//    accumulator layout a lane owns one column (here: one token) and four
+//    rows (here: head dims) of a block, and the four lanes l + 16 g share the
+//    token.  A wave's 128-row
 //    n-range is exactly one head, so the RMS reduction over the head is a
 //    register sum plus two exchanges, and both RoPE pairings keep their
 //    partners in one lane; with the operand rows staged in a fixed
@@ -38,8 +40,8 @@
 //    phases (each phase one 32-deep sub-step of all 64 accumulators), the next
 //    sub-step's fragment reads spread over the phase (a W block right after
 //    its last MFMA), and the 16 load instructions in slots without a read (a
-//    load holds the wave's issue for ~24 cycles).  MFMAs and
-//    fragment reads are written as inline assembly with explicit
+//    load holds the wave's issue for ~24 cycles).  MFMAs and fragment reads
+//    are written as inline assembly with explicit
 //    lgkmcnt waits: the buffer a read uses is only known at run time, and
 //    the compiler, unable to tell it from the buffers being loaded, would
 //    otherwise wait for every load in flight before each read.
