@@ -71,13 +71,21 @@ def parse():
 
 
 def source_hash(path: str) -> str:
-    with open(path, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    """sha256[:16] of a C++/HIP source with its comments and blank lines taken
+    out, so that a counter summary stays attached to the code it measured
+    through edits of the comments alone."""
+    import re
+    with open(path) as f:
+        text = f.read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    lines = [re.sub(r"//.*$", "", ln).rstrip() for ln in text.splitlines()]
+    code = "\n".join(ln for ln in lines if ln.strip())
+    return hashlib.sha256(code.encode()).hexdigest()[:16]
 
 
 def profile_label(path: str) -> str:
     """Where a figure read from a committed counter summary comes from."""
-    return f"{os.path.relpath(path, ROOT)} @ kernel source {source_hash(FUSED_SOURCE)}"
+    return f"{os.path.relpath(path, ROOT)} @ kernel code {source_hash(FUSED_SOURCE)}"
 
 
 def read_traffic(workload: str):
