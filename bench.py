@@ -56,7 +56,9 @@ def parse():
                    choices=["h32_u4_fused", "h56_u4", "h56_u2_fused", "h48_u8_stress"],
                    help="workload of the step (default: the 56-head Ulysses-4 shard)")
     p.add_argument("--steps", type=int, default=20)
-    p.add_argument("--warmup", type=int, default=5)
+    # 25 steps (~55 ms) let the clocks settle at this load; after 5 the first
+    # timed steps still ran 2-5 % slower
+    p.add_argument("--warmup", type=int, default=25)
     p.add_argument("--skip-cpu-baseline", action="store_true",
                    help="do not time the CPU oracle (for profiler runs)")
     p.add_argument("--cpu-seconds", type=float, default=12.0,
