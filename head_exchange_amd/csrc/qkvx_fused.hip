@@ -36,18 +36,21 @@
 //    and the wait at the end of the step leaves the W half of k+2 in flight.
 //    Within a buffer the 16-byte chunks of each row are XOR-swizzled by a
 //    function of the row, so the fragment reads are free of bank conflicts.
-//  * The main loop is a fixed sequence per K-step: 128 MFMA slots in two
-//    phases (each phase one 32-deep sub-step of all 64 accumulators), the next
-//    sub-step's fragment reads spread over the phase (a W block right after
-//    its last MFMA), and the 16 load instructions in slots without a read (a
-//    load holds the wave's issue for ~24 cycles).  MFMAs and fragment reads
-//    are written as inline assembly with explicit
-//    lgkmcnt waits: the buffer a read uses is only known at run time, and
-//    the compiler, unable to tell it from the buffers being loaded, would
+//  * The main loop is a fixed sequence per K-step: 128 MFMA slots that give
+//    each of the 64 accumulators its two 32-deep multiply-adds back to back
+//    (the chip holds a higher clock when an accumulator is written and read
+//    again at once: 6-7 % faster per kernel than one multiply-add per
+//    accumulator in turn), with the whole K-step's fragments in registers
+//    while the next K-step's fragment reads are spread over the slots (a W
+//    block right after its last MFMA), and 16 load instructions in slots
+//    without a read (a load holds the wave's issue for ~24 cycles).  MFMAs
+//    and fragment reads are written as inline assembly with explicit lgkmcnt
+//    waits: the buffer a read uses is only known at run time, and the
+//    compiler, unable to tell it from the buffers being loaded, would
 //    otherwise wait for every load in flight before each read.
 //  * Persistent: one workgroup per CU, and the K-steps of a workgroup's
 //    consecutive output tiles form one continuous load stream, so the next
-//    tile's first K-steps are in flight while the current tile's epilogue
+//    tile's first K-step is already in LDS when the current tile's epilogue
 //    runs.  The 8 XCDs (workgroup b runs on XCD b % 8) each own a run of tile
 //    rows and walk it column by column, all starting at column 0 (row bands
 //    when X is larger than the MALL): the tiles an XCD runs together share X
@@ -57,11 +60,12 @@
 //    workgroups claim tiles one at a time from per-XCD counters (then from
 //    the other XCDs' queues, the fullest first), and all XCDs finish together.
 //  * Epilogue: Q/K norm and RoPE in registers, with the weights and cos/sin
-//    values loaded one step ahead (the first before the tile's last K-step);
+//    values loaded one step ahead (the first at the epilogue's start);
 //    lanes of tokens 16 apart trade pieces so that each (nontemporal) store
 //    instruction writes whole 128-byte lines, and an m-block's stores go out
 //    together.
 #include <mutex>
+#include <type_traits>
 
 #include "qkvx_internal.h"
 
@@ -163,10 +167,6 @@ __device__ __forceinline__ float acc_read(const float& a) {
     return v;
 }
 
-template <int N>
-__device__ __forceinline__ void wait_lgkm() {
-    asm volatile("s_waitcnt lgkmcnt(%0)" ::"n"(N) : "memory");
-}
 
 // ROWS_CHECKED: M < BM, so the single tile row reads X rows past M, which must
 // come from the buffer's range check (zeros).  Otherwise the last tile row and
@@ -286,11 +286,12 @@ void fused_qkv_kernel(FusedArgs a) {
     const uint32_t ring0 = uint32_t(reinterpret_cast<uintptr_t>(ring3));
 
     f32x4 acc[8][8];
-    // fragments: the eight 16-row W blocks (A operand) of the sub-step being
-    // multiplied, each replaced by the next sub-step's block right after its
-    // last MFMA, and the eight X blocks (B operand) in two sets, the current
-    // sub-step's and the next one's
-    bf16x8 fa[7], w7[2], fb[2][8];
+    // fragments, both 32-deep sub-steps of each block: the eight 16-row W
+    // blocks (A operand) of the K-step being multiplied, blocks 0..6 each
+    // replaced by the next K-step's block right after its last MFMA and
+    // block 7 in two sets, and the eight X blocks (B operand) in two sets,
+    // the current K-step's and the next one's (200 VGPRs)
+    bf16x8 fa[7][2], fa7[2][2], fb[2][8][2];
 
     // One MFMA on accumulator (nb, mb); `init`: the tile's first product, with
     // a zero accumulator input (no separate zeroing).
@@ -303,8 +304,8 @@ void fused_qkv_kernel(FusedArgs a) {
                          : "+a"(acc[nb][mb]) : "v"(x_), "v"(y_));
     };
     // A fragment read of block blk.  Its result may only be used after a
-    // wait_lgkm that covers it: the compiler does not track it, and every use
-    // below is an MFMA placed after such a wait.
+    // wait that covers it (the compiler does not track it): every use below
+    // is an MFMA of a later period, after the closing lgkmcnt(0) wait.
     auto lds_read = [&](bf16x8& dst, uint32_t base, int blk) __attribute__((always_inline)) {
         switch (blk) {
 #define QKVX_READ(B) case B: asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(dst) \
@@ -348,106 +349,147 @@ void fused_qkv_kernel(FusedArgs a) {
     };
 
     // ---- main loop ------------------------------------------------------------
-    // K-step kt of the current tile, W half in buffer pw: two phases of 64
-    // MFMA slots (16 cycles each), slot j = 8 nb + mb.  Phase 0 multiplies the
-    // previous K-step's sub-step 1 (its fragments are in registers) and reads
-    // sub-step 0 of K-step kt; phase 1 multiplies sub-step 0 and reads
-    // sub-step 1.  In a phase, X block k of the next sub-step is read after
-    // slot 2 k + 1 (into the other X set) and W block k < 7 after slot 8 k + 7,
-    // the last MFMA of the current W block k; W block 7, read into the other
-    // of its two buffers, goes first, after slot 0.  So the last read of a
-    // phase (W block 6) leaves eight slots before the step's closing wait.
-    // Slot mb of the first row of MFMAs of a phase waits for X block mb and W
-    // block 0 of the previous phase's reads, and slot 8 for all of them.  Loads go after slots
-    // 8 k + 5: in steady steps the X half of K-step kt+1 in phase 0 and the W
-    // half of K-step kt+2 in phase 1, into the two buffers K-step kt-1 used; in
-    // a tile's first step (phase 1 only) all 16, after slots 8 k + 1 and 8 k + 5.
-    // The step ends waiting for all but the last eight loads (the W half of
-    // kt+2, which stays in flight) and for the reads, then the barrier.  A
-    // tile's first step has no phase 0: its sub-step-0 fragments are read up
-    // front and phase 1 starts the accumulators.
-    // pw: the buffer of the current step's W half.  The LDS byte addresses a
-    // step uses (its W and X buffers, phase 0's fragment-read bases, and the
-    // buffers its loads fill: lx for the X half of kt + 1, lw for the W half of
-    // kt + 2) are carried from the step before, which computes them ahead of
-    // its closing barrier: with one wave per SIMD, address arithmetic after the
-    // barrier would hold back the step's first MFMAs (20 scalar instructions
-    // there measured 1.3-1.7 % of the kernel).
+    // The K-steps of this workgroup's tiles form one stream, run in periods.
+    // In period g the MFMAs multiply K-step g-1, whose fragments (both 32-deep
+    // sub-steps of every W and X block) are in registers, while the fragment
+    // reads bring in K-step g and the loads fetch the X half of K-step g+1 and
+    // the W half of g+2 into the two buffers K-step g-1 used.  The 128 MFMA
+    // slots go row by row: slot j is W block nb = j / 16, X block
+    // mb = (j / 2) % 8, sub-step j % 2, so each accumulator takes the two
+    // multiply-adds of a K-step back to back (the chip holds a higher clock
+    // when an accumulator is written and read again at once: a loop of MFMAs,
+    // loads and fragment reads alone ran 15 % faster in this order than with
+    // one multiply-add per accumulator in turn, the whole kernel 6-7 %).
+    // Fragments: W block nb < 7 is single-buffered, its next K-step read into
+    // its registers right after the row's last MFMA (sub-step 0 after slot
+    // 16 nb + 14, sub-step 1 after 16 nb + 15); W block 7, whose row ends the
+    // period, has two register sets and is read after slots 0 and 1; the X
+    // blocks have two sets, the 16 reads of the next one after the even slots
+    // 64..98 that carry no other access.  No MFMA waits for a read: every one
+    // uses registers filled in the period before, whose end waits for all
+    // reads.  Loads go after slots 16 k + 5 and 16 k + 13: the X half in the
+    // first half of the period, the W half in the second, and the period's
+    // closing wait leaves the W half in flight.  Before the first X read a
+    // vmcnt wait makes sure the X half being read has arrived; only a tile's
+    // first period actually waits there (see upfront below).
+    // pw: the buffer of the W half the period reads (K-step g).  The LDS
+    // addresses a period uses (its W and X buffers with both sub-steps'
+    // fragment-read bases, and the buffers its loads fill: lx for the X half
+    // of g + 1, lw for the W half of g + 2) are carried from the period
+    // before, which computes them ahead of its closing barrier: with one wave
+    // per SIMD, address arithmetic after the barrier would hold back the
+    // period's first MFMAs.
     int pw = 0;
     auto buf_addr = [&](int b) { return ring0 + uint32_t(b) * (BUF_CHUNKS * 16); };
     uint32_t wb = buf_addr(0), xb = buf_addr(1), lx = buf_addr(3), lw = buf_addr(4);
-    uint32_t wa0 = wb + wl[0], xa0 = xb + xl[0];
-    auto step = [&](int kt, bool first_of_tile) __attribute__((always_inline)) {
-        // phase ph multiplies X set ph ^ 1 (phase 0: the previous K-step's
-        // sub-step 1, set 1; phase 1: sub-step 0, set 0) and reads sub-step ph
-        // into X set ph
-        auto phase = [&](const int ph, const bool init) __attribute__((always_inline)) {
-            const uint32_t wa = ph ? wb + wl[1] : wa0, xa = ph ? xb + xl[1] : xa0;
-#pragma unroll
-            for (int nb = 0; nb < 8; ++nb) {
-#pragma unroll
-                for (int mb = 0; mb < 8; ++mb) {
-                    // Row 0 waits for exactly the reads it uses, W block 0 and X
-                    // block mb of the previous phase, whose reads went out in
-                    // the order W7, X0..X3, W0, X4..X7, W1..W6 (W7 after slot 0,
-                    // X k after slot 2k+1, W k after slot 8k+7); by slot 8 the
-                    // previous phase's reads are all waited for.
-                    if (nb == 0) {
-                        if (mb == 0) wait_lgkm<10>();
-                        if (mb == 1) wait_lgkm<11>();
-                        if (mb == 2 || mb == 3 || mb == 4) wait_lgkm<12>();
-                        if (mb == 5 || mb == 6) wait_lgkm<11>();
-                        if (mb == 7) wait_lgkm<10>();
-                    }
-                    if (nb == 1 && mb == 0) wait_lgkm<6>();
-                    const bf16x8& wfr = nb < 7 ? fa[nb] : (ph ? w7[0] : w7[1]);
-                    mfma1(nb, mb, wfr, ph ? fb[0][mb] : fb[1][mb], init);
-                    const int j = 8 * nb + mb;
-                    if (j == 0) lds_read(ph ? w7[1] : w7[0], wa, 7);
-                    if ((j & 1) && j < 16) lds_read(ph ? fb[1][j >> 1] : fb[0][j >> 1], xa, j >> 1);
-                    if (mb == 7 && nb < 7) lds_read(fa[nb], wa, nb);
-                    if (mb == 5 || (init && mb == 1)) {
-                        const int v = init ? (nb * 2 + (mb == 5 ? 1 : 0)) : (ph * 8 + nb);
-                        if (v < HLOADS) load_one(false, v, kt + 1, lx);
-                        else load_one(true, v - HLOADS, kt + 2, lw);
-                    }
-                }
-            }
-        };
-        if (first_of_tile) {
-            // sub-step 0 in the order a phase reads it (W block 7 into the
-            // buffer phase 1 multiplies)
-            lds_read(w7[0], wa0, 7);
-#pragma unroll
-            for (int k = 0; k < 4; ++k) lds_read(fb[0][k], xa0, k);
-            lds_read(fa[0], wa0, 0);
-#pragma unroll
-            for (int k = 4; k < 8; ++k) lds_read(fb[0][k], xa0, k);
-#pragma unroll
-            for (int k = 1; k < 7; ++k) lds_read(fa[k], wa0, k);
-            phase(1, true);
-        } else {
-            phase(0, false);
-            phase(1, false);
-        }
-        // The next step's buffer addresses are computed before the barrier
-        // (they are operands of it), so that its first MFMAs issue right after.
-        const int pw_n = pw >= 3 ? pw - 3 : pw + 2;      // (pw + 2) % 5
+    uint32_t wa0 = wb + wl[0], wa1 = wb + wl[1], xa0 = xb + xl[0], xa1 = xb + xl[1];
+    // Closing of a period (or of a tile's up-front part): the next period's
+    // addresses, then the waits and the barrier.
+    auto advance = [&](bool wait_loads) __attribute__((always_inline)) {
+        int pw_n = pw >= 3 ? pw - 3 : pw + 2;            // (pw + 2) % 5
+        // opaque to the compiler, so that it derives the addresses from it
+        // here (a few scalar operations and four vector adds) instead of
+        // keeping every buffer's address in VGPRs through the loop
+        asm volatile("" : "+s"(pw_n));
         const int px_n = pw_n == 4 ? 0 : pw_n + 1;
         const int bx1_n = pw_n >= 2 ? pw_n - 2 : pw_n + 3;
         const int bw2_n = pw_n >= 1 ? pw_n - 1 : 4;
         const uint32_t wb_n = buf_addr(pw_n), xb_n = buf_addr(px_n);
         const uint32_t lx_n = buf_addr(bx1_n), lw_n = buf_addr(bw2_n);
-        const uint32_t wa0_n = wb_n + wl[0], xa0_n = xb_n + xl[0];
-        asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(HLOADS), "s"(wb_n),
-                     "s"(xb_n), "s"(lx_n), "s"(lw_n), "v"(wa0_n), "v"(xa0_n) : "memory");
+        const uint32_t wa0_n = wb_n + wl[0], wa1_n = wb_n + wl[1];
+        const uint32_t xa0_n = xb_n + xl[0], xa1_n = xb_n + xl[1];
+        if (wait_loads)
+            asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(HLOADS), "s"(wb_n),
+                         "s"(xb_n), "s"(lx_n), "s"(lw_n), "v"(wa0_n), "v"(wa1_n), "v"(xa0_n),
+                         "v"(xa1_n) : "memory");
+        else
+            asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::"s"(wb_n), "s"(xb_n), "s"(lx_n),
+                         "s"(lw_n), "v"(wa0_n), "v"(wa1_n), "v"(xa0_n), "v"(xa1_n) : "memory");
         pw = pw_n;
         wb = wb_n;
         xb = xb_n;
         lx = lx_n;
         lw = lw_n;
         wa0 = wa0_n;
+        wa1 = wa1_n;
         xa0 = xa0_n;
+        xa1 = xa1_n;
+    };
+    // The slot (second half of a period) after which X fragment q = 2 mb + s
+    // of the next K-step is read: the even slots 64..98 that are not a row's
+    // last two.
+    constexpr int XREAD[16] = {64, 66, 68, 70, 72, 74, 76, 80, 82, 84, 86, 88, 90, 92, 96, 98};
+    // Period j of the current tile (1 <= j < KT): multiplies K-step j - 1 from
+    // register set C (init: the tile's first K-step, zero accumulator inputs)
+    // and reads K-step j into set C ^ 1.
+    auto period = [&](auto cur, int j, auto first) __attribute__((always_inline)) {
+        constexpr int C = decltype(cur)::value;
+        constexpr bool init = decltype(first)::value;
+#pragma unroll
+        for (int nb = 0; nb < 8; ++nb) {
+#pragma unroll
+            for (int p = 0; p < 16; ++p) {
+                const int mb = p >> 1, sub = p & 1, slot = 16 * nb + p;
+                const bf16x8& afr = nb < 7 ? fa[nb][sub] : fa7[C][sub];
+                mfma1(nb, mb, afr, fb[C][mb][sub], init && sub == 0);
+                if (slot == 0) lds_read(fa7[C ^ 1][0], wa0, 7);
+                if (slot == 1) lds_read(fa7[C ^ 1][1], wa1, 7);
+                if (nb < 7 && p == 14) lds_read(fa[nb][0], wa0, nb);
+                if (nb < 7 && p == 15) lds_read(fa[nb][1], wa1, nb);
+#pragma unroll
+                for (int q = 0; q < 16; ++q)
+                    if (slot == XREAD[q]) {
+                        if (q == 0) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * HLOADS) : "memory");
+                        lds_read(fb[C ^ 1][q >> 1][q & 1], (q & 1) ? xa1 : xa0, q >> 1);
+                    }
+                if (p == 5 || p == 13) {
+                    const int v = 2 * nb + (p == 13 ? 1 : 0);
+                    if (v < HLOADS) load_one(false, v, j + 1, lx);
+                    else load_one(true, v - HLOADS, j + 2, lw);
+                }
+            }
+        }
+        advance(true);
+    };
+    // A tile's up-front part, in place of a period 0: the X half of K-step 1
+    // and the W half of K-step 2 go out (held back from the previous tile's
+    // end, whose epilogue and tile hand-off use the X buffer as a mailbox),
+    // then every fragment of K-step 0 is read into set 0; the closing barrier
+    // keeps all waves' reads ahead of period 1's loads into K-step 0's buffers.
+    // Period 1's vmcnt wait before its first X read covers the X half of
+    // K-step 1 and, as memory operations retire in order, the previous tile's
+    // stores.
+    auto upfront = [&]() __attribute__((always_inline)) {
+#pragma unroll
+        for (int i = 0; i < HLOADS; ++i) load_one(false, i, 1, lx);
+#pragma unroll
+        for (int i = 0; i < HLOADS; ++i) load_one(true, i, 2, lw);
+#pragma unroll
+        for (int nb = 0; nb < 7; ++nb) {
+            lds_read(fa[nb][0], wa0, nb);
+            lds_read(fa[nb][1], wa1, nb);
+        }
+        lds_read(fa7[0][0], wa0, 7);
+        lds_read(fa7[0][1], wa1, 7);
+#pragma unroll
+        for (int mb = 0; mb < 8; ++mb) {
+            lds_read(fb[0][mb][0], xa0, mb);
+            lds_read(fb[0][mb][1], xa1, mb);
+        }
+        advance(false);
+    };
+    // The tile's last K-step, from register set C: no reads, no loads.  The
+    // wait drains the W half of the next tile's K-step 1 (its period 1 reads it
+    // before any wait).
+    auto final_block = [&](auto cur) __attribute__((always_inline)) {
+        constexpr int C = decltype(cur)::value;
+#pragma unroll
+        for (int nb = 0; nb < 8; ++nb)
+#pragma unroll
+            for (int p = 0; p < 16; ++p)
+                mfma1(nb, p >> 1, nb < 7 ? fa[nb][p & 1] : fa7[C][p & 1], fb[C][p >> 1][p & 1],
+                      false);
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     };
 
     // ---- epilogue: one head (128 columns) per wave ----------------------------
@@ -496,22 +538,6 @@ void fused_qkv_kernel(FusedArgs a) {
             Cb[buf][i] = *reinterpret_cast<const f32x4*>(csr + off);
             Sb[buf][i] = *reinterpret_cast<const f32x4*>(csr + 64 + off);
         }
-    };
-    // The first step's (m-block 0, half 0) values of a Q/K wave's tile, issued
-    // before the tile's last K-step: that step's end-of-step wait then covers
-    // them, instead of the epilogue waiting for them behind the ring loads of
-    // the next tile (vector memory operations retire in order).
-    auto first_tables = [&](int m0, int n0) {
-        const int ncol = n0 + wn * 128;
-        if (ncol >= a.N) return;
-        const int p = ncol / a.hidden;
-        if (p == 2) return;
-        const int m_tile = m0 + wm * 128 + mfma_row(0, fi);
-        const int m = m_tile < a.M ? m_tile : a.M - 1;
-        uint32_t bidx, s;
-        a.div_s.divmod(uint32_t(m), bidx, s);
-        load_weights(p == 0 ? a.wq : a.wk);
-        load_tables(a.row0 + int(s), 0, 0);
     };
 
     auto epilogue = [&](int m0, int n0) {
@@ -602,8 +628,10 @@ void fused_qkv_kernel(FusedArgs a) {
         return;
     }
 
-    // the weights and step 0 (m-block 0, half 0) of the table are already
-    // loaded (first_tables)
+    // The weights and step 0 (m-block 0, half 0) of the table go out first:
+    // no ring loads are in flight here (the last K-step drained them and the
+    // next tile's first loads go out after the epilogue), so they wait for
+    // nothing else, and the m-block 0 sum of squares overlaps their latency.
     int rows[8], bats[8];
     bool in_range[8];
 #pragma unroll
@@ -613,6 +641,8 @@ void fused_qkv_kernel(FusedArgs a) {
         rows[mb] = br.y;
     }
     auto load_step = [&](int mb, int hp, int buf) { load_tables(rows[mb], hp, buf); };
+    load_weights(p == 0 ? a.wq : a.wk);
+    load_step(0, 0, 0);
 
 #pragma unroll
     for (int mb = 0; mb < 8; ++mb) {
@@ -695,24 +725,32 @@ void fused_qkv_kernel(FusedArgs a) {
     // claim state (thread 0 only): the queue counter being drawn from
     int cvict = xcd;
 
-    // prologue: W and X halves of K-step 0 and the W half of K-step 1
+    // prologue: W and X halves of K-step 0 and the W half of K-step 1 (the
+    // first tile's up-front part loads the X half of K-step 1 and the W half
+    // of K-step 2)
 #pragma unroll
     for (int i = 0; i < HLOADS; ++i) load_one(true, i, 0, buf_addr(0));
 #pragma unroll
     for (int i = 0; i < HLOADS; ++i) load_one(false, i, 0, buf_addr(1));
 #pragma unroll
     for (int i = 0; i < HLOADS; ++i) load_one(true, i, 1, buf_addr(2));
-    asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(HLOADS) : "memory");
+    asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+    typedef std::integral_constant<int, 0> set0;
+    typedef std::integral_constant<int, 1> set1;
+    typedef std::integral_constant<bool, true> first_step;
+    typedef std::integral_constant<bool, false> later_step;
     for (;;) {
-        step(0, true);
-        for (int kt = 1; kt < KT - 1; ++kt) step(kt, false);
-        first_tables(m0, n0);
-        step(KT - 1, false);
-        // sub-step 1 of the last K-step (its fragments arrived before the barrier)
-#pragma unroll
-        for (int nb = 0; nb < 8; ++nb)
-#pragma unroll
-            for (int mb = 0; mb < 8; ++mb) mfma1(nb, mb, nb < 7 ? fa[nb] : w7[1], fb[1][mb], false);
+        upfront();
+        // period 1 (the tile's first products), periods 2 .. KT-1 in pairs
+        // (set 1, set 0), then the last K-step from set 1: K = 128 * heads,
+        // so KT = K / 64 is even and at least 2, and every tile ends on the
+        // same code (no join of two code paths with live accumulators)
+        period(set0(), 1, first_step());
+        for (int j = 2; j < KT; j += 2) {
+            period(set1(), j, later_step());
+            period(set0(), j + 1, later_step());
+        }
+        final_block(set1());
         // the nops give the last MFMAs' results the wait states an accumulator
         // read needs
         asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
