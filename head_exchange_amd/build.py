@@ -12,6 +12,7 @@ the sanitizers; ``sanitizer_env()`` gives the environment such a run needs.
 from __future__ import annotations
 
 import os
+import re
 import shutil
 import subprocess
 import sys
@@ -33,7 +34,24 @@ FLAGS = [
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wall", "-Wno-unused-function",
     f"-I{INCLUDE}", f"-I{CSRC}",
+    # per-kernel register and scratch figures, checked after each compile
+    "-Rpass-analysis=kernel-resource-usage",
 ]
+
+_REMARK = re.compile(r"remark: +(Function Name|ScratchSize \[bytes/lane\]|VGPRs|AGPRs): (\S+)")
+
+
+def resource_usage(stderr: str) -> dict:
+    """Per-kernel {"VGPRs", "AGPRs", "ScratchSize"} from the compiler's
+    kernel-resource-usage remarks."""
+    usage, name = {}, None
+    for key, val in _REMARK.findall(stderr):
+        if key == "Function Name":
+            name = val
+            usage[name] = {}
+        elif name is not None:
+            usage[name][key.split()[0]] = int(val)
+    return usage
 
 
 def hipcc() -> str:
@@ -59,8 +77,19 @@ def _compile(src: str, verbose: bool, sanitize: bool = False) -> str:
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed on {src}:\n{r.stdout}\n{r.stderr}")
-    if verbose and r.stderr.strip():
-        print(r.stderr, file=sys.stderr)
+    # Every kernel's register plan leaves no spills: the fused kernel holds all
+    # 256 AGPRs of accumulators and ~200 VGPRs of operand fragments, and a
+    # compiler that spilled there would run the main loop through scratch
+    # memory, correct but far slower, without any other sign.
+    spills = {k: u["ScratchSize"] for k, u in resource_usage(r.stderr).items()
+              if u.get("ScratchSize", 0) > 0}
+    if spills:
+        raise RuntimeError(f"{src}: kernels spill registers to scratch memory "
+                           f"(bytes per lane): {spills}")
+    if verbose:
+        rest = "\n".join(l for l in r.stderr.splitlines() if "kernel-resource-usage" not in l)
+        if rest.strip():
+            print(rest, file=sys.stderr)
     return obj
 
 
