@@ -53,9 +53,11 @@
 //    tile's first K-step is already in LDS when the current tile's epilogue
 //    runs.  The 8 XCDs (workgroup b runs on XCD b % 8) each own a run of tile
 //    rows and walk it column by column, all starting at column 0 (row bands
-//    when X is larger than the MALL): the tiles an XCD runs together share X
-//    and W panels in its L2, and the XCDs stream the W column panels in step,
-//    so that each comes from HBM about once and is then read from the MALL.
+//    when X is larger than the MALL; in a band of few rows two or four XCDs
+//    share a run, each walking its own range of columns from that range's
+//    first): the tiles an XCD runs together share X and W panels in its L2,
+//    and the XCDs stream the W column panels in step, so that each comes
+//    from HBM about once and is then read from the MALL.
 //    Each XCD runs at its own clock under this load, so past two fixed rounds
 //    workgroups claim tiles one at a time from per-XCD counters (then from
 //    the other XCDs' queues, the fullest first), and all XCDs finish together.
@@ -203,12 +205,13 @@ void fused_qkv_kernel(FusedArgs a) {
     const bool by_xcd = G % NXCD == 0;
     const int nq = by_xcd ? NXCD : 1;
     const bool claim = a.sched != nullptr;
-    const TileOrder order(a.tiles_m, a.tiles_n, a.group_m, nq, by_xcd ? a.bands : 0,
-                          a.ready ? a.dest_cols : 0, a.part_cols);
+    TileOrder order(a.tiles_m, a.tiles_n, a.group_m, nq, by_xcd ? a.bands : 0,
+                    a.ready ? a.dest_cols : 0, a.part_cols, by_xcd ? a.csplit : 1);
+    const int xcd = by_xcd ? bid % NXCD : 0;        // the workgroup's queue
+    order.own(xcd);
     auto qlen = [&](int x) { return order.len(x); };
     // logical tile at position i < qlen(x) of queue x
     auto qtile = [&](int x, int i) { return order.logical(x, i); };
-    const int xcd = by_xcd ? bid % NXCD : 0;        // the workgroup's queue
     const int stride = by_xcd ? G / NXCD : G;       // workgroups per queue
     const int qfirst = by_xcd ? bid / NXCD : bid;   // its first position in the queue
     // Once a workgroup has claimed its last tile it counts itself finished;
@@ -913,6 +916,8 @@ hipError_t launch_fused(const FusedArgs& a_in, hipStream_t stream) {
     const int cus = a.ready && all_cus > 2 * NXCD ? all_cus - NXCD : all_cus;
     const int grid = tiles < cus ? tiles : cus;
     a.bands = lockstep_bands(a.tiles_m, a.K, BM, grid, NXCD);
+    a.csplit = lockstep_csplit(a.tiles_m, a.ready && a.dest_cols > 0 ? 3 * a.dest_cols : a.tiles_n,
+                               a.bands, grid, NXCD);
     auto kernel = a.M < BM ? (a.rope_interleaved ? fused_qkv_kernel<true, true>
                                                  : fused_qkv_kernel<true, false>)
                            : (a.rope_interleaved ? fused_qkv_kernel<false, true>

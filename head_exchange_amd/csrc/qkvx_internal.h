@@ -46,6 +46,32 @@ struct FastDiv {
 // fused projection kernel: tile order and arguments
 // ---------------------------------------------------------------------------
 
+// Quotient and remainder of small non-negative integers, 0 <= a < 2^22 and
+// 1 <= b < 2^22: a float product with the reciprocal (relative error a few
+// units of 2^-24 on the device's approximate reciprocal, so within one of the
+// exact quotient below 2^22), then one correction step each way.  The tile
+// order's index arithmetic runs in one lane between two tiles while the
+// workgroup's other waves wait, and the general 32-bit division sequence
+// there costs about a microsecond per tile.
+__host__ __device__ __forceinline__ int div_fix(int a, int b, int q) {
+    if (q * b > a) --q;
+    if ((q + 1) * b <= a) ++q;
+    return q;
+}
+__host__ __device__ __forceinline__ int small_div(int a, int b) {
+#if defined(__HIP_DEVICE_COMPILE__)
+    // the divisor is made opaque here, so that its reciprocal is computed at
+    // each use rather than hoisted out of the kernel's loops into a register
+    // held through the main loop
+    int bb = b;
+    asm volatile("" : "+v"(bb));
+    return div_fix(a, b, int(float(a) * __builtin_amdgcn_rcpf(float(bb))));
+#else
+    return div_fix(a, b, int(float(a) / float(b)));
+#endif
+}
+__host__ __device__ __forceinline__ int small_mod(int a, int b) { return a - small_div(a, b) * b; }
+
 // The order in which a fused launch runs its tiles_m x tiles_n output tiles,
 // split into nq queues (one per XCD; one for a grid that is not a multiple of
 // the XCD count).  Position i < len(x) of queue x names logical tile
@@ -56,83 +82,130 @@ struct FastDiv {
 // so that early destinations complete early; otherwise the one span is the
 // whole grid.  Within a span:
 //  * bands > 0 (XCD-lockstep): the tile rows are split into `bands` near-equal
-//    bands, run one after another.  In band b the rows are cut into nq
-//    near-equal runs; queue x owns run (x + b) % nq and walks it column by
-//    column.  Every queue starts a band at the span's first column, so the
-//    XCDs stream the W column panels in step (each comes from HBM about once
-//    per band and is then read from the MALL by the others) while the band's
-//    X rows stay in the MALL.
+//    bands, run one after another.  The queues form nq / csplit row groups of
+//    csplit queues each.  In band b the rows are cut into nq / csplit
+//    near-equal runs, and row group g owns run (g + b) % (nq / csplit); the
+//    span's columns are cut into csplit near-equal ranges, and queue x (row
+//    group x / csplit) takes range x % csplit of its group's run, walked
+//    column by column.  Every queue of a column range starts a band at the
+//    range's first column, so the XCDs stream the W column panels in step
+//    (each comes from HBM about once per band and is then read from the MALL
+//    by the others) while the band's X rows stay in the MALL.  csplit > 1
+//    serves bands of few rows: the tiles an XCD runs at once then span about
+//    as many rows as columns, which shares the most panels in its L2.
 //  * bands == 0: groups of group_m tile rows walked column by column, shared
 //    out among the queues in contiguous runs.
 struct TileOrder {
     int tiles_m, tiles_n, group_m, nq;
-    int bands;
+    int bands, csplit;
     int dest_cols, part_cols;
     int cols, span, nspan, per, rem;
+    int ng;                       // bands: row groups, nq / csplit
+    // the queue a workgroup walks (own()): its length and, for one band in
+    // one span, its row run and column range
+    int own_x = -1, own_len = 0, own_r0 = 0, own_r = 0, own_c0 = 0;
 
     __host__ __device__ TileOrder(int tm, int tn, int gm, int queues, int nbands, int dcols,
-                                  int pcols)
+                                  int pcols, int colsplit = 1)
         : tiles_m(tm), tiles_n(tn), group_m(gm), nq(queues), bands(nbands),
-          dest_cols(dcols), part_cols(pcols) {
+          csplit(colsplit > 0 ? colsplit : 1), dest_cols(dcols), part_cols(pcols) {
         cols = dcols > 0 ? 3 * dcols : tn;
         span = tm * cols;
         nspan = (tm * tn) / span;
         per = span / queues;
         rem = span % queues;
+        ng = nq / csplit;
     }
     // bands: first tile row of band b; the run of rows queue x owns in band b
-    __host__ __device__ int band_row(int b) const { return (tiles_m * b) / bands; }
+    __host__ __device__ int band_row(int b) const {
+        const int n = tiles_m * b;
+        return n < (1 << 22) ? small_div(n, bands) : n / bands;
+    }
     __host__ __device__ int own_rows(int b, int x, int& r0) const {
         const int b0 = band_row(b), rb = band_row(b + 1) - b0;
-        const int s = (x + b) % nq;
-        r0 = b0 + (rb * s) / nq;
-        return b0 + (rb * (s + 1)) / nq - r0;
+        const int s = small_mod(small_div(x, csplit) + b, ng);
+        r0 = b0 + small_div(rb * s, ng);
+        return b0 + small_div(rb * (s + 1), ng) - r0;
+    }
+    // bands: the range of span columns queue x walks
+    __host__ __device__ int own_cols(int x, int& c0) const {
+        const int c = small_mod(x, csplit);
+        c0 = small_div(cols * c, csplit);
+        return small_div(cols * (c + 1), csplit) - c0;
     }
     // positions of queue x in one span
     __host__ __device__ int span_len(int x) const {
         if (bands > 0) {
-            int rows = 0, r0;
+            int rows = 0, r0, c0;
             for (int b = 0; b < bands; ++b) rows += own_rows(b, x, r0);
-            return rows * cols;
+            return rows * own_cols(x, c0);
         }
         return per + (x < rem ? 1 : 0);
     }
-    __host__ __device__ int len(int x) const { return nspan * span_len(x); }
+    __host__ __device__ int len(int x) const {
+        return x == own_x ? own_len : nspan * span_len(x);
+    }
+    // Keeps queue x's length and (one band, one span) its row run and column
+    // range, so that its positions map to tiles with one division: a
+    // workgroup's claims are almost all in its own queue, and this index
+    // arithmetic runs in one lane between two tiles while the other waves wait.
+    // On the device x must be the same in every lane (the workgroup's queue).
+    __host__ __device__ void own(int x) {
+        own_len = nspan * span_len(x);
+        own_r = 0;
+        if (bands == 1 && nspan == 1) {
+            own_r = own_rows(0, x, own_r0);
+            own_cols(x, own_c0);
+        }
+        own_x = x;
+#if defined(__HIP_DEVICE_COMPILE__)
+        // x is the same in every lane: keep the values in scalar registers
+        own_len = __builtin_amdgcn_readfirstlane(own_len);
+        own_r = __builtin_amdgcn_readfirstlane(own_r);
+        own_r0 = __builtin_amdgcn_readfirstlane(own_r0);
+        own_c0 = __builtin_amdgcn_readfirstlane(own_c0);
+#endif
+    }
     __host__ __device__ int logical(int x, int i) const {
+        if (x == own_x && own_r > 0) {
+            const int col = small_div(i, own_r);
+            return (own_r0 + (i - col * own_r)) * cols + own_c0 + col;
+        }
         const int ln = span_len(x);
-        const int sp = i / ln;
+        const int sp = nspan > 1 ? small_div(i, ln) : 0;
         i -= sp * ln;
         if (bands > 0) {
-            int r0 = 0, r = 1;
+            int r0 = 0, r = 1, c0;
+            const int cw = own_cols(x, c0);
             for (int b = 0; b < bands; ++b) {
                 r = own_rows(b, x, r0);
-                if (i < r * cols) break;
-                i -= r * cols;
+                if (i < r * cw) break;
+                i -= r * cw;
             }
-            const int col = i / r;
-            return sp * span + (r0 + (i - col * r)) * cols + col;
+            const int col = small_div(i, r);
+            return sp * span + (r0 + (i - col * r)) * cols + c0 + col;
         }
         return sp * span + x * per + (x < rem ? x : rem) + i;
     }
     __host__ __device__ void coords(int l, int& tm, int& tn) const {
-        const int sp = l / span;
+        const int sp = nspan > 1 ? small_div(l, span) : 0;
         const int rr = l - sp * span;
         int c;
         if (bands > 0) {
-            tm = rr / cols;
+            tm = small_div(rr, cols);
             c = rr - tm * cols;
         } else {
             // groups of group_m rows, walked column by column
             const int in_group = group_m * cols;
-            const int g = rr / in_group;
+            const int g = small_div(rr, in_group);
             const int first_m = g * group_m;
             const int gsize = tiles_m - first_m < group_m ? tiles_m - first_m : group_m;
             const int r = rr - g * in_group;
-            tm = first_m + r % gsize;
-            c = r / gsize;
+            c = small_div(r, gsize);
+            tm = first_m + (r - c * gsize);
         }
         if (dest_cols > 0) {
-            const int p = c / dest_cols;
+            const int p = small_div(c, dest_cols);
             tn = p * part_cols + sp * dest_cols + (c - p * dest_cols);
         } else {
             tn = c;
@@ -156,6 +229,21 @@ inline int lockstep_bands(int tiles_m, int K, int bm, int grid, int nxcd) {
     return int((tiles_m + max_rows - 1) / max_rows);
 }
 
+// Column ranges per row run of the XCD-lockstep order (TileOrder::csplit) for
+// spans `cols` tile columns wide: the largest power of two, at most nxcd and
+// cols, that keeps the rows an XCD owns in a band at or below the square root
+// of the tiles it runs at once (grid / nxcd), so that those tiles span about
+// as many rows as columns.  1 without bands.
+inline int lockstep_csplit(int tiles_m, int cols, int bands, int grid, int nxcd) {
+    if (bands <= 0) return 1;
+    const int64_t rb = tiles_m / bands, at_once = grid / nxcd;
+    int c = 1;
+    while (2 * c <= nxcd && nxcd % (2 * c) == 0 && 2 * c <= cols &&
+           (rb * 2 * c) * (rb * 2 * c) <= at_once * int64_t(nxcd) * nxcd)
+        c *= 2;
+    return c;
+}
+
 struct FusedArgs {
     const uint16_t* x;        // [M, K] bf16
     const uint16_t* w;        // [N, K] bf16
@@ -174,6 +262,7 @@ struct FusedArgs {
     int32_t tiles_m, tiles_n;
     int32_t group_m;          // tile-row group of the grouped tile orders
     int32_t bands;            // > 0: row bands of the XCD-lockstep order (TileOrder)
+    int32_t csplit;           // column ranges per row run of that order
     int32_t rope_interleaved; // 0: pairs (i, i + 64); 1: pairs (2i, 2i + 1)
     FastDiv div_s;            // by s_local: token -> (batch, sequence row); set at launch
     float eps;

@@ -1,7 +1,8 @@
 // Host check of the fused kernel's tile order (qkvx::TileOrder, the same code
 // the kernel runs) and of its tile-claim protocol.
-//  1. For every order (XCD-lockstep bands or grouped rows, over the whole grid
-//     or destination by destination), queue count and a range of grid shapes:
+//  1. For every order (XCD-lockstep bands, with one or more column ranges per
+//     row run, or grouped rows, over the whole grid or destination by
+//     destination), queue count and a range of grid shapes:
 //     the queue positions name every logical tile exactly once, and coords()
 //     maps the logical tiles one to one onto the tile grid.
 //  2. The claim protocol, simulated with seeded random interleavings of the
@@ -10,9 +11,15 @@
 //     counter; once that queue is used up it reads every counter and claims
 //     from the queue with the most positions left, until none is left.  Every
 //     tile is run exactly once and every workgroup stops.
-//  3. lockstep_bands() on the benchmark shapes and its exclusions.
+//  3. lockstep_bands() and lockstep_csplit() on the benchmark shapes and
+//     their exclusions.
+//  4. small_div's correction step: from a quotient estimate off by the
+//     relative error of the device's approximate reciprocal (a few units of
+//     2^-24, bounded here by 2^-22), it returns the exact quotient.
 // Prints "ok <count>" or the first failure.
 #include <cstdint>
+#include <algorithm>
+#include <cmath>
 #include <cstdio>
 #include <random>
 #include <vector>
@@ -34,6 +41,17 @@ static int fails = 0;
 
 static bool covers(const TileOrder& o) {
     const int total = o.tiles_m * o.tiles_n;
+    // a workgroup's copy with its own queue kept (own()) maps every position of
+    // every queue as the plain order does
+    for (int w : {0, o.nq / 2, o.nq - 1}) {
+        TileOrder k = o;
+        k.own(w);
+        for (int x = 0; x < o.nq; ++x) {
+            if (k.len(x) != o.len(x)) return false;
+            for (int i = 0; i < o.len(x); ++i)
+                if (k.logical(x, i) != o.logical(x, i)) return false;
+        }
+    }
     std::vector<int> seen(total, 0), grid(total, 0);
     for (int x = 0; x < o.nq; ++x)
         for (int i = 0; i < o.len(x); ++i) {
@@ -125,23 +143,28 @@ int main() {
                 // bands of fewer than 8 rows leave some queues without rows in a band
                 if (nq == 8 && tm >= 8)
                     for (int b = 1; b <= 4 && b <= tm; ++b) band_counts.push_back(b);
-                for (int bands : band_counts) {
-                    const TileOrder o(tm, tn, 8, nq, bands, 0, 0);
-                    CHECK(covers(o), "order tm %d tn %d nq %d bands %d", tm, tn, nq, bands);
-                    ++checked;
-                    const int total = tm * tn;
-                    for (int G : {8, 64, 248, 256}) {
-                        int g = total < G ? total : G;
-                        if (nq == 8 && g % 8 != 0) continue;
-                        if (nq == 1 && g % 8 == 0 && g > 1) g -= 1;
-                        if (g < 1) continue;
-                        for (int rep = 0; rep < 3; ++rep) {
-                            CHECK(claims_cover(o, g, rng), "claims tm %d tn %d nq %d bands %d G %d",
-                                  tm, tn, nq, bands, g);
-                            ++checked;
+                for (int bands : band_counts)
+                    for (int cs : {1, 2, 4, 8}) {
+                        // column ranges apply to banded orders of 8 queues
+                        if (cs > 1 && (bands == 0 || cs > tn)) continue;
+                        const TileOrder o(tm, tn, 8, nq, bands, 0, 0, cs);
+                        CHECK(covers(o), "order tm %d tn %d nq %d bands %d csplit %d", tm, tn, nq,
+                              bands, cs);
+                        ++checked;
+                        const int total = tm * tn;
+                        for (int G : {8, 64, 248, 256}) {
+                            int g = total < G ? total : G;
+                            if (nq == 8 && g % 8 != 0) continue;
+                            if (nq == 1 && g % 8 == 0 && g > 1) g -= 1;
+                            if (g < 1) continue;
+                            for (int rep = 0; rep < 3; ++rep) {
+                                CHECK(claims_cover(o, g, rng),
+                                      "claims tm %d tn %d nq %d bands %d csplit %d G %d", tm, tn,
+                                      nq, bands, cs, g);
+                                ++checked;
+                            }
                         }
                     }
-                }
             }
         }
     // destination by destination (readiness words): dest_cols tile columns per
@@ -150,23 +173,25 @@ int main() {
         for (int dc : {1, 2, 3, 7})
             for (int world : {1, 2, 4, 8})
                 for (int nq : {1, 8})
-                    for (int bands = 0; bands <= 2; ++bands) {
-                        if (bands > 0 && (nq != 8 || tm < 8)) continue;
-                        const int part_cols = dc * world;
-                        const TileOrder o(tm, 3 * part_cols, 8, nq, bands, dc, part_cols);
-                        CHECK(covers(o), "dest-major tm %d dc %d world %d nq %d bands %d", tm, dc,
-                              world, nq, bands);
-                        const int total = tm * 3 * part_cols;
-                        int g = total < 248 ? total : 248;
-                        if (nq == 8) g -= g % 8;
-                        if (g >= 1) {
-                            CHECK(claims_cover(o, g, rng),
-                                  "dest-major claims tm %d dc %d world %d bands %d", tm, dc, world,
-                                  bands);
+                    for (int bands = 0; bands <= 2; ++bands)
+                        for (int cs : {1, 2, 4}) {
+                            if (bands > 0 && (nq != 8 || tm < 8)) continue;
+                            if (cs > 1 && (bands == 0 || cs > 3 * dc)) continue;
+                            const int part_cols = dc * world;
+                            const TileOrder o(tm, 3 * part_cols, 8, nq, bands, dc, part_cols, cs);
+                            CHECK(covers(o), "dest-major tm %d dc %d world %d nq %d bands %d cs %d",
+                                  tm, dc, world, nq, bands, cs);
+                            const int total = tm * 3 * part_cols;
+                            int g = total < 248 ? total : 248;
+                            if (nq == 8) g -= g % 8;
+                            if (g >= 1) {
+                                CHECK(claims_cover(o, g, rng),
+                                      "dest-major claims tm %d dc %d world %d bands %d cs %d", tm,
+                                      dc, world, bands, cs);
+                                ++checked;
+                            }
                             ++checked;
                         }
-                        ++checked;
-                    }
     // 3: band counts of the benchmark shapes (256 x 256 tiles, 256 workgroups)
     CHECK(qkvx::lockstep_bands(37, 7168, 256, 256, 8) == 1, "56-head U4 bands");
     CHECK(qkvx::lockstep_bands(74, 7168, 256, 256, 8) == 2, "56-head U2 bands");
@@ -177,7 +202,38 @@ int main() {
     CHECK(qkvx::lockstep_bands(37, 7168, 256, 250, 8) == 0, "grid not a multiple of 8");
     CHECK(qkvx::lockstep_bands(400, 8192, 256, 256, 8) == 8, "bands of at most 50 rows");
     CHECK(qkvx::lockstep_bands(9, 65536, 256, 256, 8) == 2, "bands of up to 8 rows when a row exceeds the budget");
-    checked += 9;
+    // column ranges: the 32-head shape's 16 rows in one band run as 4 x 8
+    // tiles per XCD (two ranges); the others keep one range
+    CHECK(qkvx::lockstep_csplit(16, 48, 1, 256, 8) == 2, "32-head column ranges");
+    CHECK(qkvx::lockstep_csplit(37, 84, 1, 256, 8) == 1, "56-head U4 column ranges");
+    CHECK(qkvx::lockstep_csplit(74, 84, 2, 256, 8) == 1, "56-head U2 column ranges");
+    CHECK(qkvx::lockstep_csplit(64, 72, 1, 256, 8) == 1, "48-head U8 column ranges");
+    CHECK(qkvx::lockstep_csplit(37, 84, 1, 248, 8) == 1, "readiness grid of 248");
+    CHECK(qkvx::lockstep_csplit(8, 84, 1, 256, 8) == 4, "one row per XCD");
+    CHECK(qkvx::lockstep_csplit(8, 3, 1, 256, 8) == 2, "ranges of at least one column");
+    CHECK(qkvx::lockstep_csplit(37, 84, 0, 256, 8) == 1, "no bands");
+    checked += 17;
+    // 4: the division's correction step from perturbed estimates
+    {
+        std::uniform_int_distribution<int> da(0, (1 << 22) - 1), db(1, (1 << 22) - 1);
+        auto one = [&](int a, int b) {
+            const double t = double(a) / double(b);
+            for (double e : {-1.0, 0.0, 1.0}) {
+                const int est = int(float(t * (1.0 + e * std::ldexp(1.0, -22))));
+                const int q = qkvx::div_fix(a, b, est);
+                CHECK(q == a / b, "div_fix a %d b %d est %d -> %d", a, b, est, q);
+            }
+            CHECK(qkvx::small_div(a, b) == a / b, "small_div a %d b %d", a, b);
+            ++checked;
+        };
+        for (int b = 1; b <= 600; ++b)
+            for (int k : {0, 1, 2, 7, 100, 1000, 6000})
+                for (int d : {-1, 0, 1}) {
+                    const long a = long(k) * b + d;
+                    if (a >= 0 && a < (1 << 22)) one(int(a), b);
+                }
+        for (int i = 0; i < 200000; ++i) one(da(rng), std::max(1, db(rng) >> (i % 20)));
+    }
     if (fails) {
         printf("%d failures\n", fails);
         return 1;
