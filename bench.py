@@ -46,7 +46,10 @@ def mfma_file(workload: str) -> str:
     return os.path.join(ROOT, "profiles", f"fused_qkvx_{workload}_mfma.txt")
 
 
-FUSED_SOURCE = os.path.join(ROOT, "head_exchange_amd", "csrc", "qkvx_fused.hip")
+# the fused kernel's code: its source and the internal header with its tile
+# order and argument block
+FUSED_SOURCES = tuple(os.path.join(ROOT, "head_exchange_amd", "csrc", f)
+                      for f in ("qkvx_fused.hip", "qkvx_internal.h"))
 
 
 def parse():
@@ -72,22 +75,25 @@ def parse():
     return p.parse_args()
 
 
-def source_hash(path: str) -> str:
-    """sha256[:16] of a C++/HIP source with its comments and blank lines taken
+def source_hash(paths=FUSED_SOURCES) -> str:
+    """sha256[:16] of C++/HIP sources with their comments and blank lines taken
     out, so that a counter summary stays attached to the code it measured
     through edits of the comments alone."""
     import re
-    with open(path) as f:
-        text = f.read()
-    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    lines = [re.sub(r"//.*$", "", ln).rstrip() for ln in text.splitlines()]
-    code = "\n".join(ln for ln in lines if ln.strip())
-    return hashlib.sha256(code.encode()).hexdigest()[:16]
+    h = hashlib.sha256()
+    for path in paths:
+        with open(path) as f:
+            text = f.read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        lines = [re.sub(r"//.*$", "", ln).rstrip() for ln in text.splitlines()]
+        h.update("\n".join(ln for ln in lines if ln.strip()).encode())
+        h.update(b"\0")
+    return h.hexdigest()[:16]
 
 
 def profile_label(path: str) -> str:
     """Where a figure read from a committed counter summary comes from."""
-    return f"{os.path.relpath(path, ROOT)} @ kernel code {source_hash(FUSED_SOURCE)}"
+    return f"{os.path.relpath(path, ROOT)} @ kernel code {source_hash()}"
 
 
 def read_traffic(workload: str):
@@ -101,7 +107,7 @@ def read_traffic(workload: str):
         if ":" in line and not line.startswith("#"):
             k, v = line.split(":", 1)
             kv[k.strip()] = v.strip()
-    if kv.get("kernel_source_sha256_16") != source_hash(FUSED_SOURCE):
+    if kv.get("kernel_source_sha256_16") != source_hash():
         return None
     try:
         return float(kv["hbm_bytes_per_launch"])
@@ -192,7 +198,7 @@ def read_mfma_counters(workload: str):
     if not os.path.exists(path):
         return None
     text = open(path).read()
-    if source_hash(FUSED_SOURCE) not in text:
+    if source_hash() not in text:
         return None
     kv = {}
     for line in text.splitlines():
