@@ -889,7 +889,7 @@ hipError_t launch_clear_words(unsigned int* p, int n, hipStream_t stream) {
 }
 
 // Compute units of the current device (cached per device).
-static int device_cus() {
+int device_cus() {
     static int cache[64] = {0};
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;

@@ -346,6 +346,8 @@ hipError_t launch_clear_words(unsigned int* p, int n, hipStream_t stream);
 hipError_t launch_fused(const FusedArgs& a, hipStream_t stream);
 hipError_t launch_pack(const PackArgs& a, int world, hipStream_t stream);
 hipError_t launch_band_copy(const BandCopyArgs& a, int world, hipStream_t stream);
+// Compute units of the current device (cached per device).
+int device_cus();
 // vec16: chunk and every address are multiples of 16 bytes
 hipError_t launch_chunks(const ChunkArgs& a, int world, bool vec16, hipStream_t stream);
 hipError_t launch_fill16(uint16_t* p, int64_t n, uint16_t value, hipStream_t stream);

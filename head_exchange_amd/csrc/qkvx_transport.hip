@@ -95,8 +95,13 @@ __global__ __launch_bounds__(kThreads) void pack_kernel(PackArgs a, uint32_t wor
         if (dst[k]) store_nt(dst[k], v[k]);
 }
 
-// Two vectors per thread: a workgroup copies 2 * kThreads consecutive vectors
-// of one peer, both loads in flight before the stores.  The peers are
+// VPT vectors per thread: a workgroup copies VPT * kThreads consecutive vectors
+// of one peer, all loads in flight before the stores.  Two per thread unless
+// the copy would then need more threads than the GPU holds at once and four or
+// eight would not (launch_band_copy): a copy that fits one dispatch wave runs
+// without a second, partial wave (the two-head merge chunk of the 56-head U4
+// schedule from HBM: 9.5-10.8 -> 8.1-8.8 us, level with a plain streaming copy
+// of its bytes).  The peers are
 // interleaved along the grid (peer = workgroup % world): workgroups dispatched
 // together cover the same tokens of every peer, so a token's row of the merged
 // output (or of a scatter source) is written (read) in one burst rather than in
@@ -107,8 +112,8 @@ __global__ __launch_bounds__(kThreads) void pack_kernel(PackArgs a, uint32_t wor
 // pages' merge schedules back to back: 41.5 against 47 us on the 56-head U4
 // shard, 83.5 against 96 us on the U2 shard).  From memory that no cache holds
 // both policies run within 10 % of each other.  Stores stay nontemporal.
+template <int VPT>
 __global__ __launch_bounds__(kThreads) void band_copy_kernel(BandCopyArgs a, uint32_t world) {
-    constexpr int VPT = 2;
     const uint32_t y = blockIdx.x % world;
     const uint32_t c0 = (blockIdx.x / world) * (VPT * kThreads) + threadIdx.x;
     u32x4 v[VPT];
@@ -183,8 +188,20 @@ hipError_t launch_pack(const PackArgs& a, int world, hipStream_t stream) {
 hipError_t launch_band_copy(const BandCopyArgs& a, int world, hipStream_t stream) {
     if (a.total == 0) return hipSuccess;
     const uint32_t w = uint32_t(world);
-    dim3 grid(((a.total + 2 * kThreads - 1) / (2 * kThreads)) * w);
-    hipLaunchKernelGGL(band_copy_kernel, grid, dim3(kThreads), 0, stream, a, w);
+    // threads the GPU holds at once (2048 per compute unit)
+    const uint64_t resident = uint64_t(device_cus()) * 2048u, vectors = uint64_t(a.total) * w;
+    int vpt = 2;
+    if (vectors > 2 * resident) {
+        if (vectors <= 4 * resident) vpt = 4;
+        else if (vectors <= 8 * resident) vpt = 8;
+    }
+    dim3 grid(((a.total + vpt * kThreads - 1) / (vpt * kThreads)) * w);
+    if (vpt == 8)
+        hipLaunchKernelGGL(band_copy_kernel<8>, grid, dim3(kThreads), 0, stream, a, w);
+    else if (vpt == 4)
+        hipLaunchKernelGGL(band_copy_kernel<4>, grid, dim3(kThreads), 0, stream, a, w);
+    else
+        hipLaunchKernelGGL(band_copy_kernel<2>, grid, dim3(kThreads), 0, stream, a, w);
     return hipGetLastError();
 }
 
