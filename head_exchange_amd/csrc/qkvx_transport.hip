@@ -50,15 +50,17 @@ __device__ __forceinline__ void store_nt(uint16_t* p, u32x4 v) {
 //    100 MB; its schedule 44.4 -> 34.1 us).  On the larger 56-head sources
 //    this form is 8 % slower than the next one;
 //  * fewer than 8 peers otherwise: one vector per thread, nontemporal reads,
-//    the peer is blockIdx.y;
+//    the peer is blockIdx.y; two, four or eight vectors per thread when one
+//    would need more threads than the GPU holds at once and the larger count
+//    would not, so that the copy runs in one dispatch wave (the two-head
+//    chunks of the 56-head U4 schedule: the schedule per step 139 -> 137 us);
 //  * 8 or more peers: the peer is the workgroup index modulo the peer count
 //    (workgroups dispatched together read the same tokens' rows for every
 //    peer), one vector per thread, nontemporal reads (48-head U8 schedule
 //    236 -> 212 us; with 4 peers this form is 3-4 % slower).
 // Stores are nontemporal in all three.
-template <bool PEERS_ALONG_X, bool RESIDENT>
+template <bool PEERS_ALONG_X, bool RESIDENT, int VPT>
 __global__ __launch_bounds__(kThreads) void pack_kernel(PackArgs a, uint32_t world) {
-    constexpr int VPT = RESIDENT ? 2 : 1;
     const uint32_t d = PEERS_ALONG_X ? blockIdx.x % world : blockIdx.y;
     const uint32_t c0 = (PEERS_ALONG_X ? blockIdx.x / world : blockIdx.x) * (VPT * kThreads) +
                         threadIdx.x;
@@ -169,17 +171,30 @@ __global__ __launch_bounds__(kThreads) void fill16_kernel(uint16_t* p, int64_t n
 hipError_t launch_pack(const PackArgs& a, int world, hipStream_t stream) {
     if (a.total == 0) return hipSuccess;
     const uint32_t w = uint32_t(world);
+    const uint64_t resident = uint64_t(device_cus()) * 2048u, vectors = uint64_t(a.total) * w;
     if (world >= 8) {
         const uint32_t blocks = (a.total + kThreads - 1) / kThreads;            // per peer
-        hipLaunchKernelGGL((pack_kernel<true, false>), dim3(blocks * w), dim3(kThreads), 0,
+        hipLaunchKernelGGL((pack_kernel<true, false, 1>), dim3(blocks * w), dim3(kThreads), 0,
                            stream, a, w);
     } else if (a.source_bytes <= kResidentBytes) {
         const uint32_t blocks = (a.total + 2 * kThreads - 1) / (2 * kThreads);  // per peer
-        hipLaunchKernelGGL((pack_kernel<false, true>), dim3(blocks, w), dim3(kThreads), 0,
+        hipLaunchKernelGGL((pack_kernel<false, true, 2>), dim3(blocks, w), dim3(kThreads), 0,
                            stream, a, w);
+    } else if (vectors > resident && vectors <= 8 * resident) {
+        const int vpt = vectors <= 2 * resident ? 2 : vectors <= 4 * resident ? 4 : 8;
+        const uint32_t blocks = (a.total + vpt * kThreads - 1) / (vpt * kThreads);  // per peer
+        if (vpt == 2)
+            hipLaunchKernelGGL((pack_kernel<false, false, 2>), dim3(blocks, w), dim3(kThreads), 0,
+                               stream, a, w);
+        else if (vpt == 4)
+            hipLaunchKernelGGL((pack_kernel<false, false, 4>), dim3(blocks, w), dim3(kThreads), 0,
+                               stream, a, w);
+        else
+            hipLaunchKernelGGL((pack_kernel<false, false, 8>), dim3(blocks, w), dim3(kThreads), 0,
+                               stream, a, w);
     } else {
         const uint32_t blocks = (a.total + kThreads - 1) / kThreads;            // per peer
-        hipLaunchKernelGGL((pack_kernel<false, false>), dim3(blocks, w), dim3(kThreads), 0,
+        hipLaunchKernelGGL((pack_kernel<false, false, 1>), dim3(blocks, w), dim3(kThreads), 0,
                            stream, a, w);
     }
     return hipGetLastError();
