@@ -37,7 +37,11 @@ def poison_dev(shape):
 def test_pack_into_receive_slots(gpu_lib, name):
     """Each chunk of the schedule lands in the U receive slots at rows
     rank*S_local.. exactly as the oracle places it; other rows keep the poison."""
-    wl = W.WORKLOADS[name]
+    check_pack_into_receive_slots(gpu_lib, W.WORKLOADS[name])
+
+
+def check_pack_into_receive_slots(gpu_lib, wl):
+    name = wl.name
     (q, k, v), (dq, dk, dv) = dev_sources(wl)
     B, S, U = wl.batch, wl.s_local, wl.world
     r0 = wl.rank * S
@@ -95,7 +99,11 @@ def test_merge_band_form(gpu_lib, name):
     """The attention-output band [B, S_global, H_local, 128]: source u is its
     sequence segment u; every chunk merged into a poisoned output equals the
     oracle, and each call writes only its band."""
-    wl = W.WORKLOADS[name]
+    check_merge_band_form(gpu_lib, W.WORKLOADS[name])
+
+
+def check_merge_band_form(gpu_lib, wl):
+    name = wl.name
     band = W.merge_band(wl)
     dband = to_dev(band)
     B, S, U, hl = wl.batch, wl.s_local, wl.world, wl.local_heads
@@ -109,6 +117,27 @@ def test_merge_band_form(gpu_lib, name):
                                   off, cnt, ref)
         torch.cuda.synchronize()
         assert np.array_equal(to_bits(out), ref), f"{name} chunk {chunk}"
+
+
+def test_launch_forms_by_size(gpu_lib):
+    """Chunk sizes that take every launch form of pack and merge on a 256-CU
+    GPU (more vectors per thread where that fits a copy in one dispatch wave):
+    the 56-head U4 shard with schedule [5, 4, 5] (merge chunks of 3.0 and 2.4 M
+    vectors: eight per thread) and [1, 12, 1] (pack chunk of 1.8 M vectors: four
+    per thread), and a 64-head U2 shard of 4096 tokens whose 201 MB q, k, v are
+    read nontemporally, with schedule [2, 30] (pack chunk of 0.79 M vectors:
+    two per thread).  Whole tensors, bit-exact, as in the schedule tests."""
+    base = W.WORKLOADS["h56_u4"]
+    for i, sched in ((80, (5, 4, 5)), (81, (1, 12, 1))):
+        wl = W.custom(i, batch=base.batch, s_local=base.s_local, heads=base.heads,
+                      world=base.world, rank=base.rank, layout=base.layout, schedule=sched,
+                      rope_base=base.rope_base)
+        check_merge_band_form(gpu_lib, wl)
+        if sched == (1, 12, 1):
+            check_pack_into_receive_slots(gpu_lib, wl)
+    wl = W.custom(82, batch=1, s_local=4096, heads=64, world=2, rank=1, layout="bshd",
+                  schedule=(2, 30), rope_base=1e4)
+    check_pack_into_receive_slots(gpu_lib, wl)
 
 
 def test_merge_received_form(gpu_lib):
