@@ -52,7 +52,10 @@ struct FastDiv {
 // exact quotient below 2^22), then one correction step each way.  The tile
 // order's index arithmetic runs in one lane between two tiles while the
 // workgroup's other waves wait, and the general 32-bit division sequence
-// there costs about a microsecond per tile.
+// there costs about a microsecond per tile.  Every quantity it divides there
+// (tile positions and counts, rows times queue indexes, columns) stays below
+// 2^18: the host's limits keep tokens x hidden and 3 hidden x hidden below
+// 2^31, so a launch has fewer than 2^18 tiles of 256 x 256.
 __host__ __device__ __forceinline__ int div_fix(int a, int b, int q) {
     if (q * b > a) --q;
     if ((q + 1) * b <= a) ++q;
