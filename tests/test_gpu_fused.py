@@ -207,6 +207,42 @@ def test_lockstep_order_mid_shapes(gpu_lib, wl, publish):
         assert words == sess.ready_expected() and timeouts == 0
 
 
+def random_mid_case(seed: int):
+    """A seeded random launch of 8 to 24 tile rows and 12 to 24 tile columns:
+    the XCD-lockstep order with one, two or four column ranges per row run
+    (more ranges for fewer rows), grids of all 256 compute units or of fewer
+    tiles, ragged last tile rows and columns, both layouts and pairings, and
+    readiness words on or off."""
+    rng = np.random.default_rng(9500 + seed)
+    heads = int(rng.choice([8, 10, 12, 14, 16]))
+    world = int(rng.choice([u for u in (1, 2, 4, 5, 7, 8) if heads % u == 0]))
+    batch = int(rng.integers(1, 3))
+    tokens = int(rng.integers(7 * 256 + 1, 24 * 256 + 1))
+    s_local = max(1, tokens // batch)
+    wl = W.custom(300 + seed, batch=batch, s_local=s_local, heads=heads, world=world,
+                  rank=int(rng.integers(0, world)), layout=str(rng.choice(["bshd", "fused"])),
+                  schedule=(heads // world,), rope_base=float(rng.choice([1e4, 1e6])))
+    return wl, str(rng.choice(["rotate_half", "interleaved"])), bool(rng.integers(0, 2))
+
+
+@pytest.mark.parametrize("seed", range(16))
+def test_random_mid_shapes(gpu_lib, seed):
+    wl, rope, publish = random_mid_case(seed)
+    inp = Inputs(wl)
+    sess = make_session(gpu_lib, wl, rope=rope)
+    if publish:
+        sess.set_publish(True)
+    sess.poison_receive_slots()
+    views = run(sess, inp)
+    torch.cuda.synchronize()
+    check_full(views, inp, wl.rank, f"seed {seed} {wl.name} B{wl.batch} S{wl.s_local} "
+               f"H{wl.heads} U{wl.world} r{wl.rank} {wl.layout} {rope} publish={publish}",
+               rope=rope)
+    if publish:
+        words, timeouts = sess.ready_state()
+        assert words == sess.ready_expected() and timeouts == 0
+
+
 @pytest.mark.parametrize("wl", SMALL[:3], ids=lambda w: w.name)
 def test_small_full_slots_interleaved_rope(gpu_lib, wl):
     """The pages' pairing (2i, 2i+1) selected at session creation."""
