@@ -888,21 +888,6 @@ hipError_t launch_clear_words(unsigned int* p, int n, hipStream_t stream) {
     return hipGetLastError();
 }
 
-// Compute units of the current device (cached per device).
-int device_cus() {
-    static int cache[64] = {0};
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-    if (cache[dev] == 0) {
-        int n = 0;
-        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-            n <= 0)
-            n = 256;
-        cache[dev] = n;
-    }
-    return cache[dev];
-}
-
 hipError_t launch_fused(const FusedArgs& a_in, hipStream_t stream) {
     FusedArgs a = a_in;
     a.tiles_m = (a.M + BM - 1) / BM;
